@@ -1,0 +1,85 @@
+/*
+ * norm_oracle.h -- float64 CPU oracle for the normalization family.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product library links, includes
+ * or calls this code; only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it. It shares no code, header, table or helper with
+ * the HIP kernels.
+ *
+ * Every function computes the plain mathematical definition of an operation,
+ * in double precision, with straightforward loops.  Inputs are double arrays
+ * holding the exact values the GPU path consumes (bf16 inputs are widened
+ * exactly by the caller).  All tensors are dense and contiguous:
+ *   row-wise ops:  x[M][N], normalized along the last axis;
+ *   BatchNorm:     x[Nb][C][HW] (NCHW viewed as batch, channel, spatial).
+ * Optional pointers may be NULL (weight -> 1, bias -> 0, residual -> 0,
+ * running statistics -> not updated, statistic outputs -> not written).
+ *
+ * Sources (pages, by title):
+ *   [NormPage]  "How attorch implements LayerNorm, BatchNorm and RMSNorm:
+ *                the three normalization Triton kernels explained"
+ *   [MathPage]  "Building custom GPU operators quickly with attorch.math:
+ *                an operator-fusion guide for advanced developers"
+ *   [ActPage]   "Operator fusion in practice: attorch's activation and
+ *                dropout fusion kernels"
+ */
+#ifndef NORM_ORACLE_H
+#define NORM_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_ACT_NONE = 0, ORC_ACT_RELU = 1, ORC_ACT_GELU = 2 };
+
+/* Activations and their derivatives ([ActPage] sections 5 and 6). */
+double orc_act(int act, double z);
+double orc_act_grad(int act, double z);
+/* Element-wise over an array: out = act(z), or act'(z) when grad != 0. */
+void orc_act_vec(int act, int grad, int64_t n, const double *z, double *out);
+
+/* LayerNorm ([NormPage] "LayerNorm" section). */
+void orc_ln_fwd(int64_t M, int64_t N, double eps, const double *x,
+                const double *w, const double *b, double *y, double *mean,
+                double *rstd);
+void orc_ln_bwd(int64_t M, int64_t N, double eps, const double *dy,
+                const double *x, const double *w, double *dx, double *dw,
+                double *db);
+
+/* RMSNorm ([NormPage] "RMSNorm" section). */
+void orc_rms_fwd(int64_t M, int64_t N, double eps, const double *x,
+                 const double *w, double *y, double *rstd);
+void orc_rms_bwd(int64_t M, int64_t N, double eps, const double *dy,
+                 const double *x, const double *w, double *dx, double *dw);
+
+/* BatchNorm ([NormPage] "BatchNorm" section; [MathPage] Welford + EMA). */
+void orc_bn_stats(int64_t Nb, int64_t C, int64_t HW, const double *x,
+                  double *mean, double *var_biased);
+void orc_bn_fwd_train(int64_t Nb, int64_t C, int64_t HW, double eps,
+                      double momentum, int act, const double *x,
+                      const double *res, const double *w, const double *b,
+                      double *running_mean, double *running_var, double *y,
+                      double *save_mean, double *save_rstd);
+void orc_bn_fwd_eval(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
+                     const double *x, const double *res, const double *w,
+                     const double *b, const double *running_mean,
+                     const double *running_var, double *y);
+void orc_bn_bwd(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
+                const double *dy, const double *x, const double *res,
+                const double *w, const double *b, double *dx, double *dres,
+                double *dw, double *db);
+
+/* The one-pass statistics the BatchNorm page describes, used only to show
+ * that they reach the two-pass result: Welford's per-value update, and the
+ * pairwise merge of two partial (count, mean, M2) triples. */
+void orc_welford(int64_t n, const double *x, double out[3]);
+void orc_chan_merge(const double a[3], const double b[3], double out[3]);
+
+int orc_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
