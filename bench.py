@@ -1,0 +1,392 @@
+"""Benchmark: normalization forward+backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-others] [--no-cpu]
+
+A step is one forward and one backward pass of the workload (BatchNorm
+workloads: training forward, backward, and the eval forward when the workload
+has one) on seeded synthetic inputs already resident in HBM.  Before every
+operation a 512 MiB scratch buffer is written, so inputs come from HBM rather
+than the 256 MB Infinity Cache; that flush is outside the timed spans.  Each
+operation is timed with HIP events on the stream its kernels run on; the
+main streaming kernel of the dominant operation is also bracketed by its own
+pair of HIP events through the library's timing hook.
+
+Bytes are algorithmic: what the method must move (every activation tensor in
+its I/O dtype once per pass that touches it, plus the small vectors), not
+what the hardware happened to move.  The default workload is RMSNorm bf16
+16384 x 4096; the other workloads are measured too and reported under
+"per_workload".  Rank 0 prints one JSON line.
+"""
+import argparse
+import ctypes
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "norm fwd+bwd achieved HBM GB/s (% of peak) and rows/s at 1 MI355X"
+FLUSH_BYTES = 512 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=None)
+    p.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    p.add_argument("--other-steps", type=int, default=20)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+# ------------------------------------------------------------- HIP events
+class Hip:
+    """hipEvent helpers through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+
+# ------------------------------------------------------ algorithmic bytes
+def bytes_rowwise(kind, M, N, es):
+    U = M * N * es
+    if kind == "ln":
+        fwd = 2 * U + 2 * N * es + 2 * M * 4
+        bwd = 3 * U + N * es + 2 * M * 4 + 2 * N * es
+        bwd_kernel = 3 * U + N * es + 2 * M * 4
+    else:
+        fwd = 2 * U + N * es + M * 4
+        bwd = 3 * U + N * es + M * 4 + N * es
+        bwd_kernel = 3 * U + N * es + M * 4
+    return dict(fwd=fwd, bwd=bwd, bwd_kernel=bwd_kernel, fwd_kernel=fwd)
+
+
+def bytes_bn(wl, es):
+    Nb, C, H, W = wl.shape
+    U = Nb * C * H * W * es
+    small = 8 * C * 4
+    res = 1 if wl.residual else 0
+    fwd = (2 + res + 1) * U + small          # x twice (stats, apply), res, y
+    fwd_kernel = (1 + res + 1) * U           # the apply kernel alone
+    if res:
+        bwd = 7 * U + small                  # pass 1: dy, x, res -> dres; pass 2: dres, x -> dx
+        bwd_kernel = 3 * U
+    else:
+        bwd = 5 * U + small                  # pass 1: dy, x; pass 2: dy, x -> dx
+        bwd_kernel = 3 * U
+    ev = (2 + res) * U + small if wl.eval_after_train else 0
+    return dict(fwd=fwd, bwd=bwd, eval=ev, fwd_kernel=fwd_kernel, bwd_kernel=bwd_kernel)
+
+
+# ------------------------------------------------------------ workloads
+class RowBench:
+    def __init__(self, wl, nl, torch):
+        from normalization_ln_rmsnorm_amd.workloads import gen_rowwise
+        self.wl, self.nl, self.torch = wl, nl, torch
+        M, N = wl.shape
+        self.inp = gen_rowwise(wl)
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        dev = lambda a: (torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+                         if wl.dtype == "bf16" else torch.from_numpy(a).cuda())
+        self.x, self.dy, self.w = dev(self.inp["x"]), dev(self.inp["dy"]), dev(self.inp["w"])
+        self.b = dev(self.inp["b"]) if wl.kind == "ln" else None
+        self.y = torch.empty(M, N, dtype=tdt, device="cuda")
+        self.dx = torch.empty_like(self.y)
+        self.mean = torch.empty(M, dtype=torch.float32, device="cuda")
+        self.rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+        self.dw = torch.empty(N, dtype=tdt, device="cuda")
+        self.db = torch.empty(N, dtype=tdt, device="cuda")
+        ws_fn = nl.ln_bwd_workspace_bytes if wl.kind == "ln" else nl.rms_bwd_workspace_bytes
+        self.ws = torch.empty(max(1, ws_fn(tdt, M, N)), dtype=torch.uint8, device="cuda")
+        self.bytes = bytes_rowwise(wl.kind, M, N, 2 if wl.dtype == "bf16" else 4)
+        self.ops = ["fwd", "bwd"]
+        self.dominant = "bwd"
+
+    def run(self, op):
+        nl, wl = self.nl, self.wl
+        if wl.kind == "ln":
+            if op == "fwd":
+                nl.ln_fwd(self.x, self.w, self.b, wl.eps, y=self.y, mean=self.mean, rstd=self.rstd)
+            else:
+                nl.ln_bwd(self.dy, self.x, self.w, self.mean, self.rstd, dx=self.dx, dw=self.dw,
+                          db=self.db, ws=self.ws)
+        else:
+            if op == "fwd":
+                nl.rms_fwd(self.x, self.w, wl.eps, y=self.y, rstd=self.rstd)
+            else:
+                nl.rms_bwd(self.dy, self.x, self.w, self.rstd, dx=self.dx, dw=self.dw, ws=self.ws)
+
+    def cpu_step(self, orc, arrays):
+        wl = self.wl
+        if wl.kind == "ln":
+            orc.ln_fwd(arrays["x"], arrays["w"], arrays["b"], eps=wl.eps)
+            orc.ln_bwd(arrays["dy"], arrays["x"], arrays["w"], eps=wl.eps)
+        else:
+            orc.rms_fwd(arrays["x"], arrays["w"], eps=wl.eps)
+            orc.rms_bwd(arrays["dy"], arrays["x"], arrays["w"], eps=wl.eps)
+
+
+class BnBench:
+    def __init__(self, wl, nl, torch):
+        from normalization_ln_rmsnorm_amd.workloads import gen_bn
+        self.wl, self.nl, self.torch = wl, nl, torch
+        Nb, C, H, W = wl.shape
+        inp = gen_bn(wl)
+        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        shape = (Nb, C, H, W)
+        dev = lambda a: (torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+                         if wl.dtype == "bf16" else torch.from_numpy(a).cuda())
+        self.x = dev(inp["x"]).view(shape)
+        self.dy = dev(inp["dy"]).view(shape)
+        self.res = dev(inp["res"]).view(shape) if wl.residual else None
+        self.w, self.b = dev(inp["w"]), dev(inp["b"])
+        del inp
+        self.rm = torch.zeros(C, device="cuda")
+        self.rv = torch.ones(C, device="cuda")
+        self.y = torch.empty(shape, dtype=tdt, device="cuda")
+        self.ye = torch.empty(shape, dtype=tdt, device="cuda") if wl.eval_after_train else None
+        self.dx = torch.empty(shape, dtype=tdt, device="cuda")
+        self.dres = torch.empty(shape, dtype=tdt, device="cuda") if wl.residual else None
+        self.sm = torch.empty(C, device="cuda")
+        self.sr = torch.empty(C, device="cuda")
+        self.dw = torch.empty(C, dtype=tdt, device="cuda")
+        self.db = torch.empty(C, dtype=tdt, device="cuda")
+        self.ws = torch.empty(nl.bn_workspace_bytes(tdt, Nb, C, H * W), dtype=torch.uint8, device="cuda")
+        self.bytes = bytes_bn(wl, 2 if wl.dtype == "bf16" else 4)
+        self.ops = ["fwd", "bwd"] + (["eval"] if wl.eval_after_train else [])
+        self.dominant = "bwd"
+
+    def run(self, op):
+        nl, wl = self.nl, self.wl
+        if op == "fwd":
+            nl.bn_fwd_train(self.x, self.w, self.b, self.rm, self.rv, wl.eps, wl.momentum, wl.act,
+                            self.res, y=self.y, save_mean=self.sm, save_rstd=self.sr, ws=self.ws)
+        elif op == "bwd":
+            nl.bn_bwd(self.dy, self.x, self.w, self.b, self.sm, self.sr, wl.act, self.res,
+                      dx=self.dx, dres=self.dres, dw=self.dw, db=self.db, ws=self.ws)
+        else:
+            nl.bn_fwd_eval(self.x, self.w, self.b, self.rm, self.rv, wl.eps, wl.act, self.res,
+                           y=self.ye)
+
+
+def measure(bench, steps, warmup, torch, hip, nl, flush):
+    """Times every op of `steps` steps; returns per-op and dominant-kernel ms."""
+    def one_step(record):
+        out = {}
+        for op in bench.ops:
+            flush.add_(1)
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                k0, k1 = (hip.event(), hip.event()) if op == bench.dominant else (None, None)
+                if k0 is not None:
+                    nl.arm_kernel_events(k0, k1)
+                e0.record()
+                bench.run(op)
+                e1.record()
+                out[op] = (e0, e1, k0, k1)
+            else:
+                bench.run(op)
+        return out
+
+    for _ in range(warmup):
+        one_step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    recs = [one_step(True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    op_ms = {op: [r[op][0].elapsed_time(r[op][1]) for r in recs] for op in bench.ops}
+    kern_ms = [hip.elapsed_ms(r[bench.dominant][2], r[bench.dominant][3]) for r in recs]
+    return op_ms, kern_ms, wall, nl.last_kernel_name()
+
+
+def summarize(bench, op_ms, kern_ms, steps):
+    wl = bench.wl
+    res = {"workload": wl.name, "rows": wl.rows}
+    tot_bytes, tot_ms = 0, 0.0
+    for op in bench.ops:
+        ms = float(np.mean(op_ms[op]))
+        b = bench.bytes[op]
+        res[op] = {"ms_mean": ms, "ms_p10": float(np.percentile(op_ms[op], 10)),
+                   "ms_p50": float(np.percentile(op_ms[op], 50)),
+                   "ms_p90": float(np.percentile(op_ms[op], 90)),
+                   "bytes": b, "GBps": b / ms / 1e6, "frac_of_peak": b / ms / 1e6 / PEAK_HBM_GBPS,
+                   "rows_per_s": wl.rows / (ms / 1e3)}
+        if op in ("fwd", "bwd"):
+            tot_bytes += b
+            tot_ms += ms
+    res["fwd_bwd"] = {"ms": tot_ms, "bytes": tot_bytes, "GBps": tot_bytes / tot_ms / 1e6,
+                      "frac_of_peak": tot_bytes / tot_ms / 1e6 / PEAK_HBM_GBPS,
+                      "rows_per_s": wl.rows / (tot_ms / 1e3)}
+    km = float(np.mean(kern_ms))
+    kb = bench.bytes[bench.dominant + "_kernel"]
+    res["dominant_kernel"] = {"op": bench.dominant, "avg_us": km * 1e3, "bytes": kb,
+                              "GBps": kb / km / 1e6}
+    return res
+
+
+def load_traffic(kernel_key):
+    """HBM traffic per launch recorded from rocprofv3 PMC runs, if the kernel
+    source still matches the one profiled (else None)."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.md")
+    if not os.path.exists(path):
+        return None
+    import hashlib
+    text = open(path).read()
+    m = re.search(r"```json\s*(\{.*?\})\s*```", text, flags=re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1)).get(kernel_key)
+    if not rec:
+        return None
+    src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(bench, budget_s):
+    import oracle
+    wl = bench.wl
+    bf16 = wl.dtype == "bf16"
+    if wl.kind in ("ln", "rms"):
+        arrays = {k: oracle.widen(v, bf16=bf16) if v is not None else None
+                  for k, v in bench.inp.items()}
+    else:
+        raise NotImplementedError
+    reps, spent = 0, 0.0
+    while spent < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        bench.cpu_step(oracle, arrays)
+        spent += time.perf_counter() - t0
+        reps += 1
+    per_step = spent / reps
+    tot_bytes = bench.bytes["fwd"] + bench.bytes["bwd"]
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": tot_bytes / per_step / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"the whole {wl.name} workload (fwd+bwd, float64 C oracle, OpenMP over rows), "
+                      f"{reps} repetition(s), {spent:.1f} s total; inputs pre-widened to float64",
+            "s_per_step": per_step, "rows_per_s": wl.rows / per_step, "cpu_model": model}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not "
+              "part of this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import normalization_ln_rmsnorm_amd as nl
+    from normalization_ln_rmsnorm_amd.workloads import HEADLINE, WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    nl.lib()
+    hip = Hip()
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    name = args.workload or HEADLINE
+    wl = WORKLOADS[name]
+    mk = RowBench if wl.kind in ("ln", "rms") else BnBench
+    bench = mk(wl, nl, torch)
+    op_ms, kern_ms, wall, kname = measure(bench, args.steps, args.warmup, torch, hip, nl, flush)
+    head = summarize(bench, op_ms, kern_ms, args.steps)
+    print(f"[bench] {name}: fwd {head['fwd']['ms_mean']*1e3:.1f} us  bwd {head['bwd']['ms_mean']*1e3:.1f} us  "
+          f"fwd+bwd {head['fwd_bwd']['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+
+    per = {}
+    if not args.no_others:
+        for other in WORKLOADS:
+            if other == name:
+                continue
+            ow = WORKLOADS[other]
+            b = (RowBench if ow.kind in ("ln", "rms") else BnBench)(ow, nl, torch)
+            o_ms, k_ms, _, _ = measure(b, args.other_steps, 3, torch, hip, nl, flush)
+            per[other] = summarize(b, o_ms, k_ms, args.other_steps)
+            print(f"[bench] {other}: " + "  ".join(
+                f"{op} {per[other][op]['ms_mean']*1e3:.1f} us {per[other][op]['GBps']:.0f} GB/s"
+                for op in b.ops), file=sys.stderr, flush=True)
+            del b
+            torch.cuda.empty_cache()
+
+    # Plain copy bandwidth on the same device, for context.
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cms = []
+    for _ in range(10):
+        flush.add_(1)
+        e0.record(); dst.copy_(src); e1.record(); torch.cuda.synchronize()
+        cms.append(e0.elapsed_time(e1))
+    copy_gbps = 2 * src.numel() * 4 / float(np.median(cms)) / 1e6
+    del src, dst
+
+    dk = head["dominant_kernel"]
+    traffic = load_traffic(f"{kname}|{name}")
+    roofline = {"bound": "hbm", "achieved": dk["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": dk["GBps"] / PEAK_HBM_GBPS, "traffic": traffic, "kernel": kname,
+                "bytes_per_launch": dk["bytes"], "avg_us": dk["avg_us"]}
+    fb = head["fwd_bwd"]
+    out = {
+        "metric": METRIC, "value": fb["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": fb["ms"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "op": {"rms": "RMSNorm", "ln": "LayerNorm", "bn": "BatchNorm2d"}[wl.kind] + " fwd+bwd",
+                   "shape": list(wl.shape), "io_dtype": wl.dtype, "eps": wl.eps},
+        "pct_of_peak": 100.0 * fb["frac_of_peak"], "rows_per_s": fb["rows_per_s"],
+        "fwd": head["fwd"], "bwd": head["bwd"],
+        "wall_s_timed_region_incl_flush": wall,
+        "copy_GBps": copy_gbps,
+        "roofline": roofline,
+        "per_workload": per,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(bench, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

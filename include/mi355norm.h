@@ -1,0 +1,204 @@
+/*
+ * mi355norm.h -- C ABI of the MI355X (gfx950) normalization library
+ * (libmi355norm.so): LayerNorm, RMSNorm and BatchNorm forward/backward.
+ *
+ * Operations follow three pages describing the attorch Triton kernels:
+ *   [NormPage] "How attorch implements LayerNorm, BatchNorm and RMSNorm:
+ *               the three normalization Triton kernels explained"
+ *   [MathPage] "Building custom GPU operators quickly with attorch.math:
+ *               an operator-fusion guide for advanced developers"
+ *   [ActPage]  "Operator fusion in practice: attorch's activation and
+ *               dropout fusion kernels"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every tensor pointer is a DEVICE pointer (memory from hipMalloc
+ *   or a torch CUDA tensor), to dense, contiguous, row-major storage:
+ *     row-wise ops:  x, y, dy, dx are [M][N]; w, b, dw, db are [N];
+ *                    mean, rstd are [M];
+ *     BatchNorm:     x, y, res, dy, dx, dres are NCHW, seen as [Nb][C][HW]
+ *                    (HW = H*W; HW = 1 or L gives BatchNorm1d shapes);
+ *                    w, b, dw, db, running/saved statistics are [C].
+ *   Tensors may have any alignment; 16-byte aligned tensors whose rows (or
+ *   planes) are a multiple of 16 bytes take the 128-bit vector path.
+ * Dtypes.  `dt` is the I/O dtype of x, y, dy, dx, res, dres, w, b, dw, db:
+ *   NORM_F32 (float) or NORM_BF16 (bfloat16 bit patterns).  Statistics
+ *   (mean, rstd, save_*, running_*) are always float32.  All arithmetic is
+ *   float32 with float64 for cross-workgroup merges; bf16 results are
+ *   rounded to nearest-even once, at the store.
+ * Streams.  `stream` is a hipStream_t (NULL = the legacy default stream).
+ *   Kernels are enqueued on it and the call returns without synchronizing.
+ * Ownership.  The caller allocates and owns every buffer, including the
+ *   workspace; the library never allocates, frees or synchronizes, and keeps
+ *   no state between calls.  Concurrent calls are safe if they use distinct
+ *   output and workspace buffers.  Outputs must not alias inputs.
+ * Errors.  Every entry point returns a norm_status.  Arguments are checked
+ *   on the host before anything is enqueued; on an error nothing is
+ *   launched and no output is touched.  A zero-sized problem (M == 0, or
+ *   C == 0 / Nb*HW == 0 for BatchNorm eval) is a successful no-op.  A
+ *   failed launch returns NORM_ERR_HIP.  Faults inside a kernel surface at
+ *   the caller's next synchronization, as for any stream operation.
+ */
+#ifndef MI355NORM_H
+#define MI355NORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NORM_OK = 0,
+    NORM_ERR_NULL = -1,      /* a required pointer is NULL                  */
+    NORM_ERR_SHAPE = -2,     /* a size is negative, zero where it must not  */
+                             /* be, or beyond the supported range           */
+    NORM_ERR_DTYPE = -3,     /* unknown dtype                               */
+    NORM_ERR_ACT = -4,       /* unknown activation                          */
+    NORM_ERR_ARG = -5,       /* eps < 0, momentum outside [0,1], or a       */
+                             /* BatchNorm batch of fewer than 2 values      */
+    NORM_ERR_WORKSPACE = -6, /* workspace NULL or smaller than required     */
+    NORM_ERR_HIP = -7        /* the HIP runtime rejected a launch           */
+} norm_status;
+
+typedef enum { NORM_F32 = 0, NORM_BF16 = 1 } norm_dtype;
+
+/* Activation fused after BatchNorm ([ActPage] sections 5-6; [NormPage]
+ * "BatchNorm" section): none, ReLU (derivative 0 at z <= 0), or the exact
+ * error-function GELU, z * Phi(z). */
+typedef enum { NORM_ACT_NONE = 0, NORM_ACT_RELU = 1, NORM_ACT_GELU = 2 } norm_act;
+
+/* Largest row width the row-wise kernels accept (rows are held in
+ * registers): 65536 features for bf16, 32768 for float32. */
+#define NORM_MAX_N_BF16 65536
+#define NORM_MAX_N_F32 32768
+
+/* ------------------------------------------------------------- LayerNorm
+ * Forward, [NormPage] "LayerNorm: one program normalizes a batch of rows":
+ * per row i, mean_i = sum_j x_ij / N, var_i = sum_j (x_ij - mean_i)^2 / N,
+ * rstd_i = 1/sqrt(var_i + eps), y_ij = (x_ij - mean_i) * rstd_i * w_j + b_j.
+ *   w, b      nullable (w = 1, b = 0 when NULL)
+ *   mean,rstd nullable float32 [M] outputs (the statistics saved for the
+ *             backward when training)
+ *   Requires M >= 0, 1 <= N <= NORM_MAX_N_*, eps >= 0.                   */
+norm_status ln_fwd(norm_dtype dt, int64_t M, int64_t N, float eps,
+                   const void *x, const void *w, const void *b, void *y,
+                   float *mean, float *rstd, void *stream);
+
+/* Workspace bytes ln_bwd needs for (dt, M, N) (0 when dw and db are not
+ * requested is also accepted by ln_bwd; this returns the size for both). */
+size_t ln_bwd_workspace_bytes(norm_dtype dt, int64_t M, int64_t N);
+
+/* Backward, [NormPage] "LayerNorm" section (two row sums along the feature
+ * axis, one launch for the whole row gradient) and "Engineering tricks"
+ * (weight/bias gradients as per-row-block partial sums, then a sum over
+ * the blocks).  With g = dy * w and xhat = (x - mean) * rstd:
+ *   dx = rstd * (g - mean_j(g) - xhat * mean_j(g * xhat)),
+ *   dw = sum_i dy * xhat,  db = sum_i dy.
+ *   mean, rstd  required float32 [M], as written by ln_fwd
+ *   w           nullable (treated as 1)
+ *   dw, db      nullable outputs [N] in dt; when either is non-NULL,
+ *               ws must hold ln_bwd_workspace_bytes(dt, M, N) bytes of
+ *               device memory (contents on entry are ignored).
+ * The partial sums are reduced in a fixed order: results are bitwise
+ * reproducible from run to run.                                         */
+norm_status ln_bwd(norm_dtype dt, int64_t M, int64_t N, const void *dy,
+                   const void *x, const void *w, const float *mean,
+                   const float *rstd, void *dx, void *dw, void *db, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/* --------------------------------------------------------------- RMSNorm
+ * Forward, [NormPage] "RMSNorm: LayerNorm stripped of the mean":
+ * rstd_i = 1/sqrt(sum_j x_ij^2 / N + eps), y_ij = x_ij * rstd_i * w_j.
+ *   w nullable (1); rstd nullable float32 [M] output.                     */
+norm_status rms_fwd(norm_dtype dt, int64_t M, int64_t N, float eps,
+                    const void *x, const void *w, void *y, float *rstd,
+                    void *stream);
+
+size_t rms_bwd_workspace_bytes(norm_dtype dt, int64_t M, int64_t N);
+
+/* Backward, [NormPage] "RMSNorm" section (one row sum of x * dy * w):
+ * with g = dy * w,  dx = rstd * (g - x * rstd^2 * mean_j(g * x)),
+ * dw = sum_i dy * x * rstd.  rstd required (from rms_fwd); w nullable;
+ * dw nullable, and when given ws must hold rms_bwd_workspace_bytes.      */
+norm_status rms_bwd(norm_dtype dt, int64_t M, int64_t N, const void *dy,
+                    const void *x, const void *w, const float *rstd,
+                    void *dx, void *dw, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* ------------------------------------------------------------- BatchNorm
+ * Workspace bytes for bn_fwd_train and bn_bwd at this shape (the same
+ * buffer serves both; its contents on entry are ignored).               */
+size_t bn_workspace_bytes(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW);
+
+/* Training forward, [NormPage] "BatchNorm: parallel over features +
+ * activation fusion" and [MathPage] "Practice 2: Welford + EMA".  Per
+ * channel c over its n = Nb*HW values: one-pass (Welford) statistics
+ * merged across workgroups, mean_c and biased var_c,
+ * rstd_c = 1/sqrt(var_c + eps);
+ *   z = (x - mean_c) * rstd_c * w_c + b_c (+ res),  y = act(z);
+ *   running_mean = (1 - momentum) * running_mean + momentum * mean_c,
+ *   running_var  = (1 - momentum) * running_var
+ *                  + momentum * var_c * n / (n - 1)   (unbiased, PyTorch).
+ *   res                   nullable residual, added before the activation
+ *   w, b                  nullable (1, 0)
+ *   running_mean/var      nullable float32 [C], updated in place
+ *   save_mean, save_rstd  required float32 [C] outputs (for bn_bwd)
+ *   ws                    bn_workspace_bytes(dt, Nb, C, HW) bytes
+ * Requires Nb*HW >= 2, eps >= 0, 0 <= momentum <= 1.                    */
+norm_status bn_fwd_train(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW,
+                         float eps, float momentum, norm_act act,
+                         const void *x, const void *res, const void *w,
+                         const void *b, float *running_mean,
+                         float *running_var, float *save_mean,
+                         float *save_rstd, void *y, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/* Eval forward ([NormPage] "BatchNorm" section: inference reads the
+ * running statistics): z = (x - rm_c) / sqrt(rv_c + eps) * w_c + b_c
+ * (+ res), y = act(z).  running_mean/var required; res, w, b nullable.   */
+norm_status bn_fwd_eval(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW,
+                        float eps, norm_act act, const void *x,
+                        const void *res, const void *w, const void *b,
+                        const float *running_mean, const float *running_var,
+                        void *y, void *stream);
+
+/* Backward of bn_fwd_train ([NormPage] "BatchNorm" section: the activation
+ * backward first recovers the pre-activation gradient, then the BatchNorm
+ * gradient; [ActPage] section 5 for the derivatives).  z is recomputed from
+ * x, res and the saved statistics exactly as the forward computed it;
+ *   dz = dy * act'(z);  dres = dz;  db = sum dz;  dw = sum dz * xhat;
+ *   dx = (w * rstd / n) * (n * dz - db - xhat * dw),  xhat = (x-mean)*rstd.
+ *   res, w, b      nullable, as passed to the forward
+ *   dres           required iff res is non-NULL
+ *   dw, db         nullable outputs [C]
+ *   save_mean/rstd required (from bn_fwd_train)
+ *   ws             bn_workspace_bytes(dt, Nb, C, HW) bytes.              */
+norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW,
+                   norm_act act, const void *dy, const void *x,
+                   const void *res, const void *w, const void *b,
+                   const float *save_mean, const float *save_rstd, void *dx,
+                   void *dres, void *dw, void *db, void *ws, size_t ws_bytes,
+                   void *stream);
+
+/* ------------------------------------------------------------- utilities */
+
+/* Static description of a status code (never NULL). */
+const char *norm_status_str(norm_status s);
+
+/* Timing hook for profilers and benchmarks.  Arms two caller-created
+ * hipEvent_t handles for the NEXT entry-point call made by this host
+ * thread: that call records `start` on its stream immediately before its
+ * main streaming kernel and `stop` immediately after it, then disarms.
+ * Either may be NULL to disarm.  Costs nothing when not armed.            */
+void norm_arm_kernel_events(void *start_event, void *stop_event);
+
+/* Name of the main streaming kernel the last call on this host thread
+ * launched (for matching profiler traces); "" before any launch.         */
+const char *norm_last_kernel_name(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MI355NORM_H */

@@ -1,0 +1,62 @@
+"""Build libmi355norm.so (the HIP kernels and the C ABI) for gfx950, in-tree.
+
+Each .hip file is compiled to an object in parallel, then linked into
+normalization_ln_rmsnorm_amd/libmi355norm.so.  Packed-FP32 instructions are
+disabled for the device code (-packed-fp32-ops).
+"""
+import os
+import subprocess
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(ROOT, "_build", "mi355norm")
+OUT = os.path.join(HERE, "libmi355norm.so")
+SOURCES = ["api_common.hip", "rownorm.hip", "batchnorm.hip"]
+ARCH = os.environ.get("MI355NORM_ARCH", "gfx950")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I" + os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    t0 = time.time()
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+    failed = []
+    for src, p in procs:
+        out, _ = p.communicate()
+        text = "\n".join(l for l in out.decode(errors="replace").splitlines()
+                         if "packed-fp32-ops" not in l)
+        if p.returncode != 0:
+            failed.append(src)
+            print(text, file=sys.stderr)
+        elif verbose and text.strip():
+            print(text)
+    if failed:
+        raise RuntimeError("HIP compile failed: " + ", ".join(failed))
+    tmp = OUT + ".tmp"
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, OUT)
+    if verbose:
+        print(f"built {OUT} in {time.time() - t0:.1f}s", flush=True)
+    return OUT
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,680 @@
+// batchnorm.hip -- BatchNorm training/eval forward and backward for gfx950,
+// with an optional fused residual add and ReLU / exact-GELU activation.
+//
+// Pages (by title):
+//   [NormPage] "How attorch implements LayerNorm, BatchNorm and RMSNorm:
+//               the three normalization Triton kernels explained"
+//   [MathPage] "Building custom GPU operators quickly with attorch.math:
+//               an operator-fusion guide for advanced developers"
+//   [ActPage]  "Operator fusion in practice: attorch's activation and
+//               dropout fusion kernels"
+//
+// Layout.  x is NCHW, seen as [Nb][C][HW]: the (n, c) "plane" of HW values
+// is contiguous, consecutive planes belong to consecutive channels.  A
+// channel's n = Nb*HW values are the Nb planes (0, c), (1, c), ...
+//
+// Work split.  [NormPage] "BatchNorm" section gives one program per channel
+// looping over blocks of batch x spatial values.  MI355X has 256 CUs and the
+// workloads have 64-256 channels, so here each channel is split into
+// `tiles` workgroups of `ppb` planes; every kernel's grid is C * tiles
+// workgroups, blockIdx = tile * C + c.
+//
+//   forward (training)
+//     bn_stats_kernel   one-pass statistics of each tile: every thread folds
+//                       its 128-bit chunks into a running (count, mean, M2)
+//                       with the pairwise update, merges across the wave in
+//                       float32 and across waves in float64, and writes one
+//                       float64 triple per tile ([NormPage] "BatchNorm":
+//                       online correction by the difference from the previous
+//                       mean, no second pass; [MathPage] "Practice 2").
+//     bn_merge_kernel   one wave per channel merges the tile triples in
+//                       float64, saves mean and rstd, and applies the
+//                       momentum update to the running statistics.
+//     bn_apply_kernel   z = x * a_c + s_c (+ res), y = act(z), where
+//                       a_c = w_c * rstd_c and s_c = b_c - mean_c * a_c.
+//   forward (eval)      bn_apply_kernel with mean/rstd from running stats.
+//   backward
+//     bn_bwd_reduce_kernel  recomputes z exactly as the forward did,
+//                       dz = dy * act'(z), stores dres = dz when a residual
+//                       was added, and sums dz, dz * (x - mean) and x - mean
+//                       per tile (float64 per element for float32 I/O,
+//                       float32 per thread for bf16; float64 beyond).
+//     bn_bwd_merge_kernel   one wave per channel: db = sum dz,
+//                       dw = rstd * sum dz (x - mean), and the three
+//                       coefficients of dx = k1*dz + k2*(x - mean) + k3.
+//     bn_bwd_dx_kernel  dz (re-read from dres, or recomputed from dy, x,
+//                       res), then dx.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include <initializer_list>
+#include <type_traits>
+
+#include "norm_device.hpp"
+#include "norm_host.hpp"
+
+namespace mi355norm {
+
+constexpr int kBnBlock = 256;
+constexpr int kBnWaves = kBnBlock / kWave;
+constexpr int kBnUnroll = 4;             // vectors in flight per thread per step
+constexpr int64_t kBnTileElems = 16384;  // target values per workgroup
+
+// Per-channel scale and shift shared by the forward apply and the backward
+// recompute, so both evaluate z with identical float32 operations.
+__device__ __forceinline__ void bn_coeffs(float mean, float rstd, float w, float b, float *a, float *s) {
+    *a = w * rstd;
+    *s = fmaf(-mean, *a, b);
+}
+
+// ------------------------------------------------------ pairwise statistics
+struct WelfF {
+    float n, mean, m2;
+};
+struct WelfD {
+    double n, mean, m2;
+};
+
+// Fold a chunk of `cnt` values with mean `cm` and sum of squared deviations
+// `cm2` into the running state (Chan et al. pairwise update).
+__device__ __forceinline__ void welf_fold(WelfF &s, float cnt, float cm, float cm2) {
+    const float n = s.n + cnt;
+    const float f = cnt * __builtin_amdgcn_rcpf(n);
+    const float d = cm - s.mean;
+    s.mean = fmaf(d, f, s.mean);
+    s.m2 += cm2 + d * d * (s.n * f);
+    s.n = n;
+}
+
+// Symmetric merge (identical result for merge(a,b) and merge(b,a), so every
+// lane of a butterfly holds the same value).
+__device__ __forceinline__ WelfF welf_merge(const WelfF &a, const WelfF &b) {
+    const float n = a.n + b.n;
+    if (n == 0.0f) return WelfF{0.0f, 0.0f, 0.0f};
+    const float r = __builtin_amdgcn_rcpf(n);
+    const float d = b.mean - a.mean;
+    return WelfF{n, (a.n * a.mean + b.n * b.mean) * r, (a.m2 + b.m2) + d * d * (a.n * b.n) * r};
+}
+__device__ __forceinline__ WelfD welf_merge(const WelfD &a, const WelfD &b) {
+    const double n = a.n + b.n;
+    if (n == 0.0) return WelfD{0.0, 0.0, 0.0};
+    const double d = b.mean - a.mean;
+    return WelfD{n, (a.n * a.mean + b.n * b.mean) / n, (a.m2 + b.m2) + d * d * (a.n * b.n) / n};
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+__device__ __forceinline__ WelfF wave_merge(WelfF s) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        WelfF o{shfl_xor_f(s.n, m), shfl_xor_f(s.mean, m), shfl_xor_f(s.m2, m)};
+        s = welf_merge(s, o);
+    }
+    return s;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_d(v, m);
+    return v;
+}
+
+// ------------------------------------------------------------------- tiles
+struct BnGeom {
+    int64_t Nb, HW;
+    int C, ppb, tiles;
+};
+
+__device__ __forceinline__ void tile_of_block(const BnGeom &g, int *c, int64_t *n0, int64_t *n1) {
+    *c = (int)(blockIdx.x % (unsigned)g.C);
+    const int t = (int)(blockIdx.x / (unsigned)g.C);
+    *n0 = (int64_t)t * g.ppb;
+    const int64_t e = *n0 + g.ppb;
+    *n1 = e < g.Nb ? e : g.Nb;
+}
+
+__device__ __forceinline__ int64_t plane_offset(const BnGeom &g, int64_t n, int c) {
+    return (n * g.C + c) * g.HW;
+}
+
+// -------------------------------------------------------- forward: stats
+template <typename T, int V>
+__global__ void __launch_bounds__(kBnBlock)
+bn_stats_kernel(const T *__restrict__ x, BnGeom g, double *__restrict__ part) {
+    using VT = Vec<T, V>;
+    using raw_t = typename VT::raw_t;
+    int c; int64_t n0, n1;
+    tile_of_block(g, &c, &n0, &n1);
+    const int64_t nvp = g.HW / V;  // vectors per plane
+
+    WelfF st{0.0f, 0.0f, 0.0f};
+    for (int64_t n = n0; n < n1; ++n) {
+        const T *p = x + plane_offset(g, n, c);
+        for (int64_t v0 = threadIdx.x; v0 < nvp; v0 += (int64_t)kBnBlock * kBnUnroll) {
+            raw_t r[kBnUnroll];
+#pragma unroll
+            for (int u = 0; u < kBnUnroll; ++u) {
+                const int64_t v = v0 + (int64_t)u * kBnBlock;
+                if (v < nvp) r[u] = vload_stream<T, V>(p + v * V);
+            }
+#pragma unroll
+            for (int u = 0; u < kBnUnroll; ++u) {
+                const int64_t v = v0 + (int64_t)u * kBnBlock;
+                if (v < nvp) {
+                    float f[V];
+                    VT::unpack(r[u], f);
+                    float s = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < V; ++e) s += f[e];
+                    const float cm = s * (1.0f / V);
+                    float cm2 = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        const float d = f[e] - cm;
+                        cm2 = fmaf(d, d, cm2);
+                    }
+                    welf_fold(st, (float)V, cm, cm2);
+                }
+            }
+        }
+    }
+    st = wave_merge(st);
+
+    __shared__ WelfD wave_part[kBnWaves];
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) wave_part[wave] = WelfD{st.n, st.mean, st.m2};
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        WelfD acc = wave_part[0];
+        for (int i = 1; i < kBnWaves; ++i) acc = welf_merge(acc, wave_part[i]);
+        double *dst = part + ((int64_t)c * g.tiles + blockIdx.x / (unsigned)g.C) * 3;
+        dst[0] = acc.n;
+        dst[1] = acc.mean;
+        dst[2] = acc.m2;
+    }
+}
+
+// ------------------------------------------------- forward: merge + EMA
+// One wave per channel; four channels per 256-thread block.
+__global__ void __launch_bounds__(kBnBlock)
+bn_merge_kernel(const double *__restrict__ part, int C, int tiles, float eps, float momentum,
+                float *__restrict__ running_mean, float *__restrict__ running_var,
+                float *__restrict__ save_mean, float *__restrict__ save_rstd) {
+    const int c = blockIdx.x * kBnWaves + threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    if (c >= C) return;  // whole wave exits together
+    WelfD acc{0.0, 0.0, 0.0};
+    for (int t = lane; t < tiles; t += kWave) {
+        const double *q = part + ((int64_t)c * tiles + t) * 3;
+        acc = welf_merge(acc, WelfD{q[0], q[1], q[2]});
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        WelfD o{shfl_xor_d(acc.n, m), shfl_xor_d(acc.mean, m), shfl_xor_d(acc.m2, m)};
+        acc = welf_merge(acc, o);
+    }
+    if (lane == 0) {
+        const double n = acc.n;
+        const double var = acc.m2 / n;  // biased: the normalization variance
+        save_mean[c] = (float)acc.mean;
+        save_rstd[c] = (float)(1.0 / sqrt(var + (double)eps));
+        // [MathPage] "Practice 2": new = (1 - momentum) * old + momentum * batch;
+        // the running variance takes the unbiased batch variance.
+        const double m = (double)momentum;
+        if (running_mean) running_mean[c] = (float)((1.0 - m) * running_mean[c] + m * acc.mean);
+        if (running_var) running_var[c] = (float)((1.0 - m) * running_var[c] + m * (acc.m2 / (n - 1.0)));
+    }
+}
+
+// ---------------------------------------------------- forward: apply
+// MODE 0: statistics from save_mean/save_rstd (training);
+// MODE 1: from running_mean/running_var with eps (eval).
+template <typename T, int V, int ACT, bool RES, int MODE>
+__global__ void __launch_bounds__(kBnBlock)
+bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__restrict__ w,
+                const T *__restrict__ b, const float *__restrict__ stat_mean,
+                const float *__restrict__ stat_scale, float eps, T *__restrict__ y, BnGeom g) {
+    using VT = Vec<T, V>;
+    using raw_t = typename VT::raw_t;
+    int c; int64_t n0, n1;
+    tile_of_block(g, &c, &n0, &n1);
+    const float mean = stat_mean[c];
+    const float rstd = MODE == 0 ? stat_scale[c] : 1.0f / sqrtf(stat_scale[c] + eps);
+    float a, s;
+    bn_coeffs(mean, rstd, w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a, &s);
+    const int64_t nvp = g.HW / V;
+
+    for (int64_t n = n0; n < n1; ++n) {
+        const int64_t off = plane_offset(g, n, c);
+        for (int64_t v0 = threadIdx.x; v0 < nvp; v0 += (int64_t)kBnBlock * kBnUnroll) {
+            raw_t rx[kBnUnroll], rr[kBnUnroll];
+#pragma unroll
+            for (int u = 0; u < kBnUnroll; ++u) {
+                const int64_t v = v0 + (int64_t)u * kBnBlock;
+                if (v < nvp) {
+                    rx[u] = vload_stream<T, V>(x + off + v * V);
+                    if (RES) rr[u] = vload_stream<T, V>(res + off + v * V);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kBnUnroll; ++u) {
+                const int64_t v = v0 + (int64_t)u * kBnBlock;
+                if (v < nvp) {
+                    float f[V], rf[V], o[V];
+                    VT::unpack(rx[u], f);
+                    if (RES) VT::unpack(rr[u], rf);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        float z = fmaf(f[e], a, s);
+                        if (RES) z += rf[e];
+                        o[e] = act_fwd<ACT>(z);
+                    }
+                    vstore_stream<T, V>(y + off + v * V, VT::pack(o));
+                }
+            }
+        }
+    }
+}
+
+// --------------------------------------------------- backward: pass 1
+template <typename T, int V, int ACT, bool RES>
+__global__ void __launch_bounds__(kBnBlock)
+bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__restrict__ res,
+                     const T *__restrict__ w, const T *__restrict__ b,
+                     const float *__restrict__ save_mean, const float *__restrict__ save_rstd,
+                     T *__restrict__ dres, BnGeom g, double *__restrict__ part) {
+    using VT = Vec<T, V>;
+    using raw_t = typename VT::raw_t;
+    int c; int64_t n0, n1;
+    tile_of_block(g, &c, &n0, &n1);
+    const float mean = save_mean[c];
+    float a, s;
+    bn_coeffs(mean, save_rstd[c], w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a, &s);
+    const int64_t nvp = g.HW / V;
+
+    // Per-element accumulation type: float64 for float32 I/O (x - mean and
+    // dz * (x - mean) are then exact, which the 1e-5 tolerance on the
+    // channel sums needs when a channel's dw lands near zero), float32 per
+    // thread for bf16 I/O (ample for bf16 outputs).  Threads and tiles are
+    // always combined in float64.  The third sum, of x - mean, corrects for
+    // the saved mean being rounded to float32.
+    using Acc = typename std::conditional<sizeof(T) == 4, double, float>::type;
+    Acc s_dz = 0, s_dzx = 0, s_xc = 0;
+    const Acc mean_a = (Acc)mean;
+    for (int64_t n = n0; n < n1; ++n) {
+        const int64_t off = plane_offset(g, n, c);
+        for (int64_t v0 = threadIdx.x; v0 < nvp; v0 += (int64_t)kBnBlock * kBnUnroll) {
+            raw_t rd[kBnUnroll], rx[kBnUnroll], rr[kBnUnroll];
+#pragma unroll
+            for (int u = 0; u < kBnUnroll; ++u) {
+                const int64_t v = v0 + (int64_t)u * kBnBlock;
+                if (v < nvp) {
+                    rd[u] = vload_stream<T, V>(dy + off + v * V);
+                    rx[u] = vload_stream<T, V>(x + off + v * V);
+                    if (RES && ACT != kActNone) rr[u] = vload_stream<T, V>(res + off + v * V);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kBnUnroll; ++u) {
+                const int64_t v = v0 + (int64_t)u * kBnBlock;
+                if (v < nvp) {
+                    float df[V], xf[V], rf[V], dz[V];
+                    VT::unpack(rd[u], df);
+                    VT::unpack(rx[u], xf);
+                    if (RES && ACT != kActNone) VT::unpack(rr[u], rf);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        if (ACT != kActNone) {
+                            float z = fmaf(xf[e], a, s);
+                            if (RES) z += rf[e];
+                            dz[e] = df[e] * act_grad<ACT>(z);
+                        } else {
+                            dz[e] = df[e];
+                        }
+                        const Acc xc = (Acc)xf[e] - mean_a;
+                        const Acc d = (Acc)dz[e];
+                        s_dz += d;
+                        s_dzx = fma(d, xc, s_dzx);
+                        s_xc += xc;
+                    }
+                    if (RES) vstore_stream<T, V>(dres + off + v * V, VT::pack(dz));
+                }
+            }
+        }
+    }
+    const double t_dz = wave_sum_d((double)s_dz);
+    const double t_dzx = wave_sum_d((double)s_dzx);
+    const double t_xc = wave_sum_d((double)s_xc);
+    __shared__ double wave_part[kBnWaves][3];
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        wave_part[wave][0] = t_dz;
+        wave_part[wave][1] = t_dzx;
+        wave_part[wave][2] = t_xc;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double p0 = 0.0, p1 = 0.0, p2 = 0.0;
+        for (int i = 0; i < kBnWaves; ++i) {
+            p0 += wave_part[i][0];
+            p1 += wave_part[i][1];
+            p2 += wave_part[i][2];
+        }
+        double *dst = part + ((int64_t)c * g.tiles + blockIdx.x / (unsigned)g.C) * 3;
+        dst[0] = p0;
+        dst[1] = p1;
+        dst[2] = p2;
+    }
+}
+
+// ----------------------------------------------------- backward: merge
+// With m the saved (float32) mean, the tile sums are S_dz = sum dz,
+// S_dzx = sum dz (x - m) and S_xc = sum (x - m).  The exact batch mean is
+// m + S_xc / n, so
+//   db = S_dz,   dw = rstd * (S_dzx - S_xc * S_dz / n)   (= sum dz * xhat)
+// and dx = (w rstd / n)(n dz - db - xhat dw) = k1 dz + k2 (x - m) + k3 with
+//   k1 = w rstd,  k2 = -w rstd^2 dw / n,  k3 = -w rstd db / n - k2 S_xc / n.
+template <typename T>
+__global__ void __launch_bounds__(kBnBlock)
+bn_bwd_merge_kernel(const double *__restrict__ part, int C, int tiles, double n_total,
+                    const T *__restrict__ w, const float *__restrict__ save_rstd,
+                    T *__restrict__ dw, T *__restrict__ db, float *__restrict__ coef) {
+    const int c = blockIdx.x * kBnWaves + threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    if (c >= C) return;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0;
+    for (int t = lane; t < tiles; t += kWave) {
+        const double *q = part + ((int64_t)c * tiles + t) * 3;
+        s0 += q[0];
+        s1 += q[1];
+        s2 += q[2];
+    }
+    s0 = wave_sum_d(s0);
+    s1 = wave_sum_d(s1);
+    s2 = wave_sum_d(s2);
+    if (lane == 0) {
+        const double r = (double)save_rstd[c];
+        const double wc = w ? (double)ld1(w + c) : 1.0;
+        const double mean_shift = s2 / n_total;  // exact mean minus saved mean
+        const double dbeta = s0;
+        const double dgamma = r * (s1 - mean_shift * s0);
+        if (db) st1(db + c, (float)dbeta);
+        if (dw) st1(dw + c, (float)dgamma);
+        const double k2 = -wc * r * r * dgamma / n_total;
+        coef[c * 4 + 0] = (float)(wc * r);
+        coef[c * 4 + 1] = (float)k2;
+        coef[c * 4 + 2] = (float)(-wc * r * dbeta / n_total - k2 * mean_shift);
+        coef[c * 4 + 3] = 0.0f;
+    }
+}
+
+// ----------------------------------------------------- backward: pass 2
+// DZ_SRC 0: dz = dy (no activation, no residual recompute needed);
+//        1: dz re-read from dres (written by pass 1, exact in float32);
+//        2: dz recomputed from dy, x (and res) as in pass 1.
+template <typename T, int V, int ACT, bool RES, int DZ_SRC>
+__global__ void __launch_bounds__(kBnBlock)
+bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__restrict__ res,
+                 const T *__restrict__ dres, const T *__restrict__ w, const T *__restrict__ b,
+                 const float *__restrict__ save_mean, const float *__restrict__ save_rstd,
+                 const float *__restrict__ coef, T *__restrict__ dx, BnGeom g) {
+    using VT = Vec<T, V>;
+    using raw_t = typename VT::raw_t;
+    int c; int64_t n0, n1;
+    tile_of_block(g, &c, &n0, &n1);
+    const float mean = save_mean[c];
+    float a = 0.0f, s = 0.0f;
+    if (DZ_SRC == 2) bn_coeffs(mean, save_rstd[c], w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a, &s);
+    const float k1 = coef[c * 4 + 0], k2 = coef[c * 4 + 1], k3 = coef[c * 4 + 2];
+    const int64_t nvp = g.HW / V;
+    const T *dzsrc = DZ_SRC == 1 ? dres : dy;
+
+    for (int64_t n = n0; n < n1; ++n) {
+        const int64_t off = plane_offset(g, n, c);
+        for (int64_t v0 = threadIdx.x; v0 < nvp; v0 += (int64_t)kBnBlock * kBnUnroll) {
+            raw_t rd[kBnUnroll], rx[kBnUnroll], rr[kBnUnroll];
+#pragma unroll
+            for (int u = 0; u < kBnUnroll; ++u) {
+                const int64_t v = v0 + (int64_t)u * kBnBlock;
+                if (v < nvp) {
+                    rd[u] = vload_stream<T, V>(dzsrc + off + v * V);
+                    rx[u] = vload_stream<T, V>(x + off + v * V);
+                    if (DZ_SRC == 2 && RES) rr[u] = vload_stream<T, V>(res + off + v * V);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kBnUnroll; ++u) {
+                const int64_t v = v0 + (int64_t)u * kBnBlock;
+                if (v < nvp) {
+                    float df[V], xf[V], rf[V], o[V];
+                    VT::unpack(rd[u], df);
+                    VT::unpack(rx[u], xf);
+                    if (DZ_SRC == 2 && RES) VT::unpack(rr[u], rf);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        float dz = df[e];
+                        if (DZ_SRC == 2 && ACT != kActNone) {
+                            float z = fmaf(xf[e], a, s);
+                            if (RES) z += rf[e];
+                            dz = df[e] * act_grad<ACT>(z);
+                        }
+                        o[e] = fmaf(k1, dz, fmaf(k2, xf[e] - mean, k3));
+                    }
+                    vstore_stream<T, V>(dx + off + v * V, VT::pack(o));
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- host side
+static BnGeom make_geom(int64_t Nb, int64_t C, int64_t HW) {
+    BnGeom g;
+    g.Nb = Nb;
+    g.HW = HW;
+    g.C = (int)C;
+    int64_t ppb = HW > 0 ? ceil_div(kBnTileElems, HW) : 1;
+    if (ppb > Nb) ppb = Nb > 0 ? Nb : 1;
+    if (ppb < 1) ppb = 1;
+    g.ppb = (int)ppb;
+    g.tiles = (int)(Nb > 0 ? ceil_div(Nb, ppb) : 1);
+    return g;
+}
+
+static norm_status check_bn(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW) {
+    if (!dtype_ok(dt)) return NORM_ERR_DTYPE;
+    if (Nb < 0 || C < 0 || HW < 0) return NORM_ERR_SHAPE;
+    if (C > (int64_t)1 << 24 || Nb > (int64_t)1 << 31 || HW > (int64_t)1 << 40) return NORM_ERR_SHAPE;
+    if (C > 0 && Nb > 0 && HW > 0 && Nb * C > ((int64_t)1 << 31) - 1) return NORM_ERR_SHAPE;
+    return NORM_OK;
+}
+
+static bool bn_vec_ok(norm_dtype dt, int64_t HW, std::initializer_list<const void *> ptrs) {
+    if ((HW * (int64_t)dtype_size(dt)) % 16 != 0) return false;
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return false;
+    return true;
+}
+
+static size_t ws_layout(int64_t Nb, int64_t C, int64_t HW, size_t *coef_off) {
+    const BnGeom g = make_geom(Nb, C, HW);
+    const size_t fwd = (size_t)C * g.tiles * 3 * sizeof(double);
+    const size_t bwd_part = (size_t)C * g.tiles * 3 * sizeof(double);
+    const size_t coef_at = (bwd_part + 255) & ~(size_t)255;
+    const size_t bwd = coef_at + (size_t)C * 4 * sizeof(float);
+    if (coef_off) *coef_off = coef_at;
+    return fwd > bwd ? fwd : bwd;
+}
+
+template <typename T, int V>
+static norm_status launch_fwd_train(const BnGeom &g, hipStream_t st, norm_act act, float eps, float momentum,
+                                    const void *x, const void *res, const void *w, const void *b,
+                                    float *rm, float *rv, float *sm, float *sr, void *y, void *ws) {
+    const dim3 grid((unsigned)(g.C * (int64_t)g.tiles));
+    double *part = static_cast<double *>(ws);
+    hipLaunchKernelGGL((bn_stats_kernel<T, V>), grid, dim3(kBnBlock), 0, st, (const T *)x, g, part);
+    hipLaunchKernelGGL(bn_merge_kernel, dim3((unsigned)ceil_div(g.C, kBnWaves)), dim3(kBnBlock), 0, st,
+                       (const double *)part, g.C, g.tiles, eps, momentum, rm, rv, sm, sr);
+    using fn_t = void (*)(const T *, const T *, const T *, const T *, const float *, const float *, float, T *, BnGeom);
+    fn_t fn = nullptr;
+    const bool r = res != nullptr;
+    switch (act) {
+    case NORM_ACT_NONE: fn = r ? bn_apply_kernel<T, V, kActNone, true, 0> : bn_apply_kernel<T, V, kActNone, false, 0>; break;
+    case NORM_ACT_RELU: fn = r ? bn_apply_kernel<T, V, kActRelu, true, 0> : bn_apply_kernel<T, V, kActRelu, false, 0>; break;
+    case NORM_ACT_GELU: fn = r ? bn_apply_kernel<T, V, kActGelu, true, 0> : bn_apply_kernel<T, V, kActGelu, false, 0>; break;
+    }
+    hook_before(st, "bn_apply_kernel<train>");
+    hipLaunchKernelGGL(fn, grid, dim3(kBnBlock), 0, st, (const T *)x, (const T *)res, (const T *)w, (const T *)b,
+                       (const float *)sm, (const float *)sr, eps, (T *)y, g);
+    hook_after(st);
+    return launch_status();
+}
+
+template <typename T, int V>
+static norm_status launch_fwd_eval(const BnGeom &g, hipStream_t st, norm_act act, float eps, const void *x,
+                                   const void *res, const void *w, const void *b, const float *rm,
+                                   const float *rv, void *y) {
+    const dim3 grid((unsigned)(g.C * (int64_t)g.tiles));
+    using fn_t = void (*)(const T *, const T *, const T *, const T *, const float *, const float *, float, T *, BnGeom);
+    fn_t fn = nullptr;
+    const bool r = res != nullptr;
+    switch (act) {
+    case NORM_ACT_NONE: fn = r ? bn_apply_kernel<T, V, kActNone, true, 1> : bn_apply_kernel<T, V, kActNone, false, 1>; break;
+    case NORM_ACT_RELU: fn = r ? bn_apply_kernel<T, V, kActRelu, true, 1> : bn_apply_kernel<T, V, kActRelu, false, 1>; break;
+    case NORM_ACT_GELU: fn = r ? bn_apply_kernel<T, V, kActGelu, true, 1> : bn_apply_kernel<T, V, kActGelu, false, 1>; break;
+    }
+    hook_before(st, "bn_apply_kernel<eval>");
+    hipLaunchKernelGGL(fn, grid, dim3(kBnBlock), 0, st, (const T *)x, (const T *)res, (const T *)w, (const T *)b,
+                       rm, rv, eps, (T *)y, g);
+    hook_after(st);
+    return launch_status();
+}
+
+template <typename T, int V, int ACT>
+static void launch_bwd_act(const BnGeom &g, hipStream_t st, bool has_res, const void *dy, const void *x,
+                           const void *res, const void *w, const void *b, const float *sm, const float *sr,
+                           void *dx, void *dres, void *dw, void *db, void *ws, size_t coef_off) {
+    const dim3 grid((unsigned)(g.C * (int64_t)g.tiles));
+    double *part = static_cast<double *>(ws);
+    float *coef = reinterpret_cast<float *>(static_cast<char *>(ws) + coef_off);
+    if (has_res)
+        hipLaunchKernelGGL((bn_bwd_reduce_kernel<T, V, ACT, true>), grid, dim3(kBnBlock), 0, st, (const T *)dy,
+                           (const T *)x, (const T *)res, (const T *)w, (const T *)b, sm, sr, (T *)dres, g, part);
+    else
+        hipLaunchKernelGGL((bn_bwd_reduce_kernel<T, V, ACT, false>), grid, dim3(kBnBlock), 0, st, (const T *)dy,
+                           (const T *)x, (const T *)res, (const T *)w, (const T *)b, sm, sr, (T *)dres, g, part);
+    hipLaunchKernelGGL(bn_bwd_merge_kernel<T>, dim3((unsigned)ceil_div(g.C, kBnWaves)), dim3(kBnBlock), 0, st,
+                       (const double *)part, g.C, g.tiles, (double)g.Nb * (double)g.HW, (const T *)w, sr, (T *)dw,
+                       (T *)db, coef);
+    // dz for pass 2: float32 dres holds dz exactly; bf16 dres is rounded, so
+    // there dz is recomputed from dy and x (and res).
+    const bool fp32 = sizeof(T) == 4;
+    hook_before(st, "bn_bwd_dx_kernel");
+    if (ACT == kActNone && !has_res) {
+        hipLaunchKernelGGL((bn_bwd_dx_kernel<T, V, ACT, false, 0>), grid, dim3(kBnBlock), 0, st, (const T *)dy,
+                           (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr,
+                           (const float *)coef, (T *)dx, g);
+    } else if (has_res && (fp32 || ACT == kActNone)) {
+        hipLaunchKernelGGL((bn_bwd_dx_kernel<T, V, ACT, true, 1>), grid, dim3(kBnBlock), 0, st, (const T *)dy,
+                           (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr,
+                           (const float *)coef, (T *)dx, g);
+    } else if (has_res) {
+        hipLaunchKernelGGL((bn_bwd_dx_kernel<T, V, ACT, true, 2>), grid, dim3(kBnBlock), 0, st, (const T *)dy,
+                           (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr,
+                           (const float *)coef, (T *)dx, g);
+    } else {
+        hipLaunchKernelGGL((bn_bwd_dx_kernel<T, V, ACT, false, 2>), grid, dim3(kBnBlock), 0, st, (const T *)dy,
+                           (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr,
+                           (const float *)coef, (T *)dx, g);
+    }
+    hook_after(st);
+}
+
+template <typename T, int V>
+static norm_status launch_bwd(const BnGeom &g, hipStream_t st, norm_act act, const void *dy, const void *x,
+                              const void *res, const void *w, const void *b, const float *sm, const float *sr,
+                              void *dx, void *dres, void *dw, void *db, void *ws, size_t coef_off) {
+    const bool r = res != nullptr;
+    switch (act) {
+    case NORM_ACT_NONE: launch_bwd_act<T, V, kActNone>(g, st, r, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws, coef_off); break;
+    case NORM_ACT_RELU: launch_bwd_act<T, V, kActRelu>(g, st, r, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws, coef_off); break;
+    case NORM_ACT_GELU: launch_bwd_act<T, V, kActGelu>(g, st, r, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws, coef_off); break;
+    }
+    return launch_status();
+}
+
+static bool act_ok(norm_act a) { return a == NORM_ACT_NONE || a == NORM_ACT_RELU || a == NORM_ACT_GELU; }
+
+}  // namespace mi355norm
+
+using namespace mi355norm;
+
+extern "C" size_t bn_workspace_bytes(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW) {
+    if (check_bn(dt, Nb, C, HW) != NORM_OK) return 0;
+    return ws_layout(Nb, C, HW, nullptr);
+}
+
+extern "C" norm_status bn_fwd_train(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, float eps, float momentum,
+                                    norm_act act, const void *x, const void *res, const void *w, const void *b,
+                                    float *running_mean, float *running_var, float *save_mean, float *save_rstd,
+                                    void *y, void *ws, size_t ws_bytes, void *stream) {
+    norm_status s = check_bn(dt, Nb, C, HW);
+    if (s != NORM_OK) return s;
+    if (!act_ok(act)) return NORM_ERR_ACT;
+    if (!(eps >= 0.0f) || !(momentum >= 0.0f && momentum <= 1.0f)) return NORM_ERR_ARG;
+    if (C == 0) return NORM_OK;
+    if (Nb * HW < 2) return NORM_ERR_ARG;  // the unbiased running variance needs n >= 2
+    if (!x || !y || !save_mean || !save_rstd) return NORM_ERR_NULL;
+    if (!ws || ws_bytes < ws_layout(Nb, C, HW, nullptr)) return NORM_ERR_WORKSPACE;
+    const BnGeom g = make_geom(Nb, C, HW);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool vec = bn_vec_ok(dt, HW, {x, res, y});
+    if (dt == NORM_F32)
+        return vec ? launch_fwd_train<float, 4>(g, st, act, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws)
+                   : launch_fwd_train<float, 1>(g, st, act, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws);
+    return vec ? launch_fwd_train<bf16_t, 8>(g, st, act, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws)
+               : launch_fwd_train<bf16_t, 1>(g, st, act, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws);
+}
+
+extern "C" norm_status bn_fwd_eval(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, float eps, norm_act act,
+                                   const void *x, const void *res, const void *w, const void *b,
+                                   const float *running_mean, const float *running_var, void *y, void *stream) {
+    norm_status s = check_bn(dt, Nb, C, HW);
+    if (s != NORM_OK) return s;
+    if (!act_ok(act)) return NORM_ERR_ACT;
+    if (!(eps >= 0.0f)) return NORM_ERR_ARG;
+    if (C == 0 || Nb * HW == 0) return NORM_OK;
+    if (!x || !y || !running_mean || !running_var) return NORM_ERR_NULL;
+    const BnGeom g = make_geom(Nb, C, HW);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool vec = bn_vec_ok(dt, HW, {x, res, y});
+    if (dt == NORM_F32)
+        return vec ? launch_fwd_eval<float, 4>(g, st, act, eps, x, res, w, b, running_mean, running_var, y)
+                   : launch_fwd_eval<float, 1>(g, st, act, eps, x, res, w, b, running_mean, running_var, y);
+    return vec ? launch_fwd_eval<bf16_t, 8>(g, st, act, eps, x, res, w, b, running_mean, running_var, y)
+               : launch_fwd_eval<bf16_t, 1>(g, st, act, eps, x, res, w, b, running_mean, running_var, y);
+}
+
+extern "C" norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, norm_act act, const void *dy,
+                              const void *x, const void *res, const void *w, const void *b, const float *save_mean,
+                              const float *save_rstd, void *dx, void *dres, void *dw, void *db, void *ws,
+                              size_t ws_bytes, void *stream) {
+    norm_status s = check_bn(dt, Nb, C, HW);
+    if (s != NORM_OK) return s;
+    if (!act_ok(act)) return NORM_ERR_ACT;
+    if (C == 0) return NORM_OK;
+    if (Nb * HW < 2) return NORM_ERR_ARG;
+    if (!dy || !x || !dx || !save_mean || !save_rstd) return NORM_ERR_NULL;
+    if (res && !dres) return NORM_ERR_NULL;
+    size_t coef_off = 0;
+    if (!ws || ws_bytes < ws_layout(Nb, C, HW, &coef_off)) return NORM_ERR_WORKSPACE;
+    const BnGeom g = make_geom(Nb, C, HW);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool vec = bn_vec_ok(dt, HW, {dy, x, res, dx, dres});
+    if (dt == NORM_F32)
+        return vec ? launch_bwd<float, 4>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws, coef_off)
+                   : launch_bwd<float, 1>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws, coef_off);
+    return vec ? launch_bwd<bf16_t, 8>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws, coef_off)
+               : launch_bwd<bf16_t, 1>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws, coef_off);
+}

@@ -1,0 +1,185 @@
+// norm_device.hpp -- device-side building blocks for the gfx950 kernels:
+// element I/O (float32 / bf16, 128-bit vectors), wave64 reductions (DPP,
+// ds_swizzle, readlane), and the activation functions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355norm {
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- dtypes
+// bf16 is carried as its 16-bit pattern.  Widening is exact (the pattern is
+// the top half of a float32); narrowing uses gfx950's v_cvt_pk_bf16_f32,
+// which rounds to nearest-even.
+struct bf16_t {
+    uint16_t bits;
+};
+
+typedef __bf16 hw_bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float hw_f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    hw_f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, hw_bf16x2));
+}
+
+// Vec<T, V>: V consecutive elements of type T moved by one load/store
+// instruction, unpacked into V floats.  V * sizeof(T) is 16 bytes on the
+// vector path and sizeof(T) on the scalar path.
+template <typename T, int V> struct Vec;
+
+template <> struct Vec<float, 4> {
+    static constexpr int n = 4;
+    using raw_t = u32x4;
+    __device__ __forceinline__ static void unpack(const raw_t &r, float *f) {
+        f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y);
+        f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+    }
+    __device__ __forceinline__ static raw_t pack(const float *f) {
+        return raw_t{__float_as_uint(f[0]), __float_as_uint(f[1]),
+                     __float_as_uint(f[2]), __float_as_uint(f[3])};
+    }
+};
+
+template <> struct Vec<float, 1> {
+    static constexpr int n = 1;
+    using raw_t = uint32_t;
+    __device__ __forceinline__ static void unpack(const raw_t &r, float *f) { f[0] = __uint_as_float(r); }
+    __device__ __forceinline__ static raw_t pack(const float *f) { return __float_as_uint(f[0]); }
+};
+
+template <> struct Vec<bf16_t, 8> {
+    static constexpr int n = 8;
+    using raw_t = u32x4;
+    __device__ __forceinline__ static void unpack(const raw_t &r, float *f) {
+        f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x); f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
+        f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z); f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
+    }
+    __device__ __forceinline__ static raw_t pack(const float *f) {
+        return raw_t{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                     pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+    }
+};
+
+template <> struct Vec<bf16_t, 1> {
+    static constexpr int n = 1;
+    using raw_t = uint16_t;
+    __device__ __forceinline__ static void unpack(const raw_t &r, float *f) {
+        f[0] = __uint_as_float(uint32_t(r) << 16);
+    }
+    __device__ __forceinline__ static raw_t pack(const float *f) {
+        return raw_t(pack_bf16x2(f[0], 0.0f) & 0xffffu);
+    }
+};
+
+// Vector loads and stores.  `p` points at element 0 of the vector.
+template <typename T, int V>
+__device__ __forceinline__ typename Vec<T, V>::raw_t vload(const T *p) {
+    return *reinterpret_cast<const typename Vec<T, V>::raw_t *>(p);
+}
+template <typename T, int V>
+__device__ __forceinline__ void vstore(T *p, const typename Vec<T, V>::raw_t &r) {
+    *reinterpret_cast<typename Vec<T, V>::raw_t *>(p) = r;
+}
+// Streaming variants: the data is touched once, so mark it non-temporal.
+template <typename T, int V>
+__device__ __forceinline__ typename Vec<T, V>::raw_t vload_stream(const T *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const typename Vec<T, V>::raw_t *>(p));
+}
+template <typename T, int V>
+__device__ __forceinline__ void vstore_stream(T *p, const typename Vec<T, V>::raw_t &r) {
+    __builtin_nontemporal_store(r, reinterpret_cast<typename Vec<T, V>::raw_t *>(p));
+}
+
+// Scalar parameter load (w, b, statistics) widened to float.
+__device__ __forceinline__ float ld1(const float *p) { return *p; }
+__device__ __forceinline__ float ld1(const bf16_t *p) { return __uint_as_float(uint32_t(p->bits) << 16); }
+__device__ __forceinline__ void st1(float *p, float v) { *p = v; }
+__device__ __forceinline__ void st1(bf16_t *p, float v) { p->bits = uint16_t(pack_bf16x2(v, 0.0f) & 0xffffu); }
+
+// ------------------------------------------------------- wave reductions
+// DPP control codes (gfx9 encoding).
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;       // lane i <- lane 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float swz_xor16(float v) {
+    // ds_swizzle bit mode: and_mask 0x1f, or_mask 0, xor_mask 0x10.
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+__device__ __forceinline__ float lane_read(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over aligned groups of `seg` lanes (seg a power of two, 1..64); every
+// lane of a group receives the group's sum.  All 64 lanes must be active.
+// The combining order depends only on lane positions, so results are
+// reproducible.  `seg` is wave-uniform, so its tests are scalar branches.
+__device__ __forceinline__ float seg_sum(float v, int seg) {
+    if (seg > 1) v += dpp<kDppXor1>(v);
+    if (seg > 2) v += dpp<kDppXor2>(v);
+    if (seg > 4) v += dpp<kDppHalfMirror>(v);
+    if (seg > 8) v += dpp<kDppMirror>(v);
+    if (seg > 16) v += swz_xor16(v);
+    if (seg > 32) v = lane_read(v, 0) + lane_read(v, 32);
+    return v;
+}
+
+// Two sums at once (keeps the dependency chains interleaved).
+__device__ __forceinline__ void seg_sum2(float &a, float &b, int seg) {
+    if (seg > 1) { a += dpp<kDppXor1>(a); b += dpp<kDppXor1>(b); }
+    if (seg > 2) { a += dpp<kDppXor2>(a); b += dpp<kDppXor2>(b); }
+    if (seg > 4) { a += dpp<kDppHalfMirror>(a); b += dpp<kDppHalfMirror>(b); }
+    if (seg > 8) { a += dpp<kDppMirror>(a); b += dpp<kDppMirror>(b); }
+    if (seg > 16) { a += swz_xor16(a); b += swz_xor16(b); }
+    if (seg > 32) {
+        a = lane_read(a, 0) + lane_read(a, 32);
+        b = lane_read(b, 0) + lane_read(b, 32);
+    }
+}
+
+// Full-wave butterfly on doubles through ds_bpermute (used once per
+// workgroup in the BatchNorm reductions, where float64 accumulation keeps
+// the channel sums exact enough).
+__device__ __forceinline__ double shfl_xor_d(double v, int mask) {
+    return __shfl_xor(v, mask, kWave);
+}
+
+// ------------------------------------------------------------ activations
+// ReLU and the exact error-function GELU ([ActPage] sections 5-6), computed
+// in float32.  GELU(z) = z * Phi(z), Phi(z) = (1 + erf(z / sqrt 2)) / 2;
+// GELU'(z) = Phi(z) + z * phi(z), phi(z) = exp(-z^2 / 2) / sqrt(2 pi).
+enum Act : int { kActNone = 0, kActRelu = 1, kActGelu = 2 };
+
+constexpr float kInvSqrt2 = 0.70710678118654752440f;
+constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
+
+template <int ACT> __device__ __forceinline__ float act_fwd(float z) {
+    if constexpr (ACT == kActRelu) return z > 0.0f ? z : 0.0f;
+    else if constexpr (ACT == kActGelu) return 0.5f * z * (1.0f + erff(z * kInvSqrt2));
+    else return z;
+}
+
+template <int ACT> __device__ __forceinline__ float act_grad(float z) {
+    if constexpr (ACT == kActRelu) return z > 0.0f ? 1.0f : 0.0f;
+    else if constexpr (ACT == kActGelu) {
+        float Phi = 0.5f * (1.0f + erff(z * kInvSqrt2));
+        float phi = expf(-0.5f * z * z) * kInvSqrt2Pi;
+        return fmaf(z, phi, Phi);
+    } else return 1.0f;
+}
+
+}  // namespace mi355norm

@@ -1,0 +1,602 @@
+// rownorm.hip -- LayerNorm and RMSNorm forward/backward for gfx950.
+//
+// Pages (by title):
+//   [NormPage] "How attorch implements LayerNorm, BatchNorm and RMSNorm:
+//               the three normalization Triton kernels explained"
+//
+// Design.  Every row is normalized by a group of `tpr` threads (a power of
+// two from 1 to 1024) that holds the whole row in registers: thread `l` of
+// the group owns the 128-bit vectors l, l + tpr, l + 2*tpr, ... (IT of them),
+// so each load instruction of a wave reads consecutive 16-byte chunks.  The
+// row sums are reduced inside the wave with DPP / ds_swizzle / readlane and,
+// when a row spans several waves, combined through LDS in a fixed order.
+// Blocks are persistent: each walks rows blockIdx*rpb, +grid*rpb, ... so the
+// weight (and bias) vectors are loaded once per block and kept in registers.
+// Nothing here is a dense contraction; the kernels are bound by HBM traffic
+// (read x, write y forward; read x and dy, write dx backward).
+//
+// Backward.  dx needs two row sums ([NormPage] "LayerNorm" section:
+// mean_j(g) and mean_j(g * xhat)); RMSNorm needs only the second
+// ([NormPage] "RMSNorm" section).  The weight/bias gradients are column sums
+// over rows: each thread accumulates its own columns over the rows its block
+// visits, the row slots of a block are combined in LDS, and each block
+// writes one partial row to the workspace ([NormPage] "Engineering tricks":
+// per-row-block partials followed by a sum).  A second kernel adds the
+// partial rows in a fixed order (float64), so dw/db are reproducible.
+#include <hip/hip_runtime.h>
+
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <initializer_list>
+
+#include "norm_device.hpp"
+#include "norm_host.hpp"
+
+namespace mi355norm {
+
+constexpr int kMaxWavesPerBlock = 16;
+constexpr int kMaxBwdBlocksPerCU = 8;  // cap on persistent backward blocks per CU
+
+template <typename VT> __device__ __forceinline__ typename VT::raw_t ones_raw() {
+    float f[VT::n];
+#pragma unroll
+    for (int e = 0; e < VT::n; ++e) f[e] = 1.0f;
+    return VT::pack(f);
+}
+template <typename VT> __device__ __forceinline__ typename VT::raw_t zeros_raw() {
+    float f[VT::n];
+#pragma unroll
+    for (int e = 0; e < VT::n; ++e) f[e] = 0.0f;
+    return VT::pack(f);
+}
+
+// Sum of `v` over the threads of one row group.  `slot` alternates between
+// two LDS areas so that back-to-back reductions need one barrier each.
+__device__ __forceinline__ float row_sum(float v, int tpr, float (*lds)[kMaxWavesPerBlock], int slot) {
+    v = seg_sum(v, tpr < kWave ? tpr : kWave);
+    if (tpr > kWave) {  // block-uniform: the row spans tpr/64 waves
+        const int wave = threadIdx.x / kWave;
+        if ((threadIdx.x & (kWave - 1)) == 0) lds[slot][wave] = v;
+        __syncthreads();
+        const int wpr = tpr / kWave;
+        const int first = (wave / wpr) * wpr;
+        float s = 0.0f;
+        for (int i = 0; i < wpr; ++i) s += lds[slot][first + i];
+        v = s;
+    }
+    return v;
+}
+
+__device__ __forceinline__ void row_sum2(float &a, float &b, int tpr, float (*lds)[kMaxWavesPerBlock][2], int slot) {
+    seg_sum2(a, b, tpr < kWave ? tpr : kWave);
+    if (tpr > kWave) {
+        const int wave = threadIdx.x / kWave;
+        if ((threadIdx.x & (kWave - 1)) == 0) {
+            lds[slot][wave][0] = a;
+            lds[slot][wave][1] = b;
+        }
+        __syncthreads();
+        const int wpr = tpr / kWave;
+        const int first = (wave / wpr) * wpr;
+        float sa = 0.0f, sb = 0.0f;
+        for (int i = 0; i < wpr; ++i) {
+            sa += lds[slot][first + i][0];
+            sb += lds[slot][first + i][1];
+        }
+        a = sa;
+        b = sb;
+    }
+}
+
+// ------------------------------------------------------------------ forward
+// LayerNorm ([NormPage] "LayerNorm" section): mean, then the sum of squared
+// deviations (exact two-pass over the register-resident row), rstd by rsqrt,
+// y = (x - mean) * rstd * w + b.  RMSNorm ([NormPage] "RMSNorm" section):
+// no mean; rstd from the mean of squares; y = x * rstd * w.
+template <typename T, int V, int IT, bool RMS, int MAXB>
+__global__ void __launch_bounds__(MAXB)
+row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
+               T *__restrict__ y, float *__restrict__ mean_out, float *__restrict__ rstd_out,
+               int64_t M, int N, float inv_n, float eps, int tpr) {
+    using VT = Vec<T, V>;
+    using raw_t = typename VT::raw_t;
+    __shared__ float lds[2][kMaxWavesPerBlock];
+
+    const int nv = N / V;
+    const int lane = threadIdx.x & (tpr - 1);
+    const int rpb = blockDim.x / tpr;
+    const int slot_in_block = threadIdx.x / tpr;
+
+    raw_t wr[IT], br[IT];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int v = lane + k * tpr;
+        wr[k] = ones_raw<VT>();
+        br[k] = zeros_raw<VT>();
+        if (v < nv) {
+            if (w) wr[k] = vload<T, V>(w + (int64_t)v * V);
+            if (!RMS && b) br[k] = vload<T, V>(b + (int64_t)v * V);
+        }
+    }
+
+    for (int64_t base = (int64_t)blockIdx.x * rpb; base < M; base += (int64_t)gridDim.x * rpb) {
+        const int64_t row = base + slot_in_block;
+        const bool active = row < M;
+        const T *xrow = x + row * N;
+
+        float xf[IT][V];
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int v = lane + k * tpr;
+            raw_t r = zeros_raw<VT>();
+            if (active && v < nv) r = vload_stream<T, V>(xrow + (int64_t)v * V);
+            VT::unpack(r, xf[k]);
+        }
+
+        float mean = 0.0f;
+        if (!RMS) {
+            float s = 0.0f;
+#pragma unroll
+            for (int k = 0; k < IT; ++k)
+#pragma unroll
+                for (int e = 0; e < V; ++e) s += xf[k][e];
+            mean = row_sum(s, tpr, lds, 0) * inv_n;
+        }
+        float q = 0.0f;
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const bool valid = lane + k * tpr < nv;
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float d = xf[k][e] - mean;
+                q += valid ? d * d : 0.0f;
+            }
+        }
+        const float rstd = rsqrtf(row_sum(q, tpr, lds, 1) * inv_n + eps);
+
+        if (active) {
+            T *yrow = y + row * N;
+#pragma unroll
+            for (int k = 0; k < IT; ++k) {
+                const int v = lane + k * tpr;
+                if (v < nv) {
+                    float wf[V], bf[V], o[V];
+                    VT::unpack(wr[k], wf);
+                    VT::unpack(br[k], bf);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) o[e] = (xf[k][e] - mean) * rstd * wf[e] + bf[e];
+                    vstore_stream<T, V>(yrow + (int64_t)v * V, VT::pack(o));
+                }
+            }
+            if (lane == 0) {
+                if (!RMS && mean_out) mean_out[row] = mean;
+                if (rstd_out) rstd_out[row] = rstd;
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------- backward
+// With g = dy * w and xhat = (x - mean) * rstd (RMSNorm: xhat = x * rstd):
+//   LayerNorm  dx = rstd * (g - mean_j(g) - xhat * mean_j(g * xhat))
+//   RMSNorm    dx = rstd * (g - xhat * mean_j(g * xhat))
+// (for RMSNorm, x * rstd^2 * mean_j(g * x) = xhat * mean_j(g * xhat)).
+// Column partials: dw += dy * xhat, db += dy, per thread, then per block.
+template <typename T, int V, int IT, bool RMS, int MAXB>
+__global__ void __launch_bounds__(MAXB)
+row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__restrict__ w,
+               const float *__restrict__ mean_in, const float *__restrict__ rstd_in,
+               T *__restrict__ dx, float *__restrict__ part_w, float *__restrict__ part_b,
+               int64_t M, int N, float inv_n, int tpr) {
+    using VT = Vec<T, V>;
+    using raw_t = typename VT::raw_t;
+    __shared__ float lds[2][kMaxWavesPerBlock][2];
+
+    const int nv = N / V;
+    const int lane = threadIdx.x & (tpr - 1);
+    const int rpb = blockDim.x / tpr;
+    const int slot_in_block = threadIdx.x / tpr;
+
+    raw_t wr[IT];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int v = lane + k * tpr;
+        wr[k] = ones_raw<VT>();
+        if (w && v < nv) wr[k] = vload<T, V>(w + (int64_t)v * V);
+    }
+
+    float acc_w[IT][V], acc_b[IT][V];
+#pragma unroll
+    for (int k = 0; k < IT; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc_w[k][e] = acc_b[k][e] = 0.0f;
+
+    int slot = 0;
+    for (int64_t base = (int64_t)blockIdx.x * rpb; base < M; base += (int64_t)gridDim.x * rpb) {
+        const int64_t row = base + slot_in_block;
+        const bool active = row < M;
+
+        float xf[IT][V], gf[IT][V];
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int v = lane + k * tpr;
+            raw_t rx = zeros_raw<VT>(), rd = zeros_raw<VT>();
+            if (active && v < nv) {
+                rx = vload_stream<T, V>(x + row * N + (int64_t)v * V);
+                rd = vload_stream<T, V>(dy + row * N + (int64_t)v * V);
+            }
+            VT::unpack(rx, xf[k]);
+            VT::unpack(rd, gf[k]);  // dy for now; g after the weight product
+        }
+        const float mean = (!RMS && active) ? mean_in[row] : 0.0f;
+        const float rstd = active ? rstd_in[row] : 0.0f;
+
+        float s_gx = 0.0f, s_g = 0.0f;
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            float wf[V];
+            VT::unpack(wr[k], wf);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float d = gf[k][e];
+                const float xh = (xf[k][e] - mean) * rstd;
+                acc_w[k][e] += d * xh;
+                if (!RMS) acc_b[k][e] += d;
+                const float g = d * wf[e];
+                xf[k][e] = xh;
+                gf[k][e] = g;
+                s_gx += g * xh;
+                s_g += g;
+            }
+        }
+        // Out-of-range elements hold x = dy = 0, so they add nothing above;
+        // for LayerNorm xhat of a padded element is -mean*rstd but its g is 0.
+        if (RMS) s_g = 0.0f;
+        row_sum2(s_gx, s_g, tpr, lds, slot);
+        slot ^= 1;
+        const float c_gx = s_gx * inv_n, c_g = s_g * inv_n;
+
+        if (active) {
+            T *dxrow = dx + row * N;
+#pragma unroll
+            for (int k = 0; k < IT; ++k) {
+                const int v = lane + k * tpr;
+                if (v < nv) {
+                    float o[V];
+#pragma unroll
+                    for (int e = 0; e < V; ++e) o[e] = rstd * (gf[k][e] - c_g - xf[k][e] * c_gx);
+                    vstore_stream<T, V>(dxrow + (int64_t)v * V, VT::pack(o));
+                }
+            }
+        }
+    }
+
+    // Combine the row slots of this block column by column and write one
+    // partial row per block.  LDS layout [element][thread] avoids bank
+    // conflicts; slots are added in increasing order.
+    if (part_w == nullptr && part_b == nullptr) return;
+    if (rpb == 1) {  // one row slot: every thread owns distinct columns
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int v = lane + k * tpr;
+            if (v >= nv) continue;
+            const int64_t off = (int64_t)blockIdx.x * N + (int64_t)v * V;
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                if (part_w) part_w[off + e] = acc_w[k][e];
+                if (part_b) part_b[off + e] = acc_b[k][e];
+            }
+        }
+        return;
+    }
+    extern __shared__ float colbuf[];  // blockDim.x * V floats
+    for (int which = 0; which < 2; ++which) {
+        float *part = which == 0 ? part_w : part_b;
+        if (part == nullptr) continue;
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int v = lane + k * tpr;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                colbuf[e * blockDim.x + threadIdx.x] = which == 0 ? acc_w[k][e] : acc_b[k][e];
+            __syncthreads();
+            if (slot_in_block == 0 && v < nv) {
+                float o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    float s = 0.0f;
+                    for (int r = 0; r < rpb; ++r) s += colbuf[e * blockDim.x + r * tpr + threadIdx.x];
+                    o[e] = s;
+                }
+                float *dst = part + (int64_t)blockIdx.x * N + (int64_t)v * V;
+#pragma unroll
+                for (int e = 0; e < V; ++e) dst[e] = o[e];
+            }
+        }
+    }
+}
+
+// Column sums of G partial rows (float64, fixed order) -> dw / db in T.
+// blockDim = (64, 4): 64 columns per block, 4 interleaved row groups.
+template <typename T>
+__global__ void __launch_bounds__(256)
+colsum_kernel(const float *__restrict__ part_w, const float *__restrict__ part_b, int G, int N,
+              T *__restrict__ dw, T *__restrict__ db) {
+    __shared__ double red[4][64];
+    const float *part = blockIdx.y == 0 ? part_w : part_b;
+    T *out = blockIdx.y == 0 ? dw : db;
+    if (part == nullptr || out == nullptr) return;  // uniform per block
+    const int col = blockIdx.x * 64 + threadIdx.x;
+    double s = 0.0;
+    if (col < N)
+        for (int g = threadIdx.y; g < G; g += 4) s += (double)part[(int64_t)g * N + col];
+    red[threadIdx.y][threadIdx.x] = s;
+    __syncthreads();
+    if (threadIdx.y == 0 && col < N) {
+        double t = red[0][threadIdx.x] + red[1][threadIdx.x];
+        t += red[2][threadIdx.x];
+        t += red[3][threadIdx.x];
+        st1(out + col, (float)t);
+    }
+}
+
+// Zero fill (used for parameter gradients of an empty batch; a kernel rather
+// than a memset so the call stays safe under stream capture).
+template <typename T>
+__global__ void zero_fill_kernel(T *__restrict__ out, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) st1(out + i, 0.0f);
+}
+
+// ---------------------------------------------------------------- planning
+struct RowPlan {
+    int vec = 1;    // elements per vector access
+    int it = 1;     // vectors per thread
+    int tpr = 1;    // threads per row
+    int block = 64; // threads per block
+    int grid = 1;   // persistent blocks
+};
+
+static const int kVecIts[] = {1, 2, 3, 4, 6, 8};
+static const int kScalarIts[] = {1, 2, 4, 8, 16, 32, 64};
+
+// Optional tuning override for experiments: MI355NORM_ROW_PLAN="tpr,it,blocks_per_cu".
+static bool env_override(int *tpr, int *it, int *bpc) {
+    const char *s = getenv("MI355NORM_ROW_PLAN");
+    if (!s || !*s) return false;
+    int a = 0, b = 0, c = 0;
+    if (sscanf(s, "%d,%d,%d", &a, &b, &c) != 3) return false;
+    *tpr = a; *it = b; *bpc = c;
+    return true;
+}
+
+static bool make_plan(norm_dtype dt, int64_t M, int64_t N, bool vec_ok, bool backward, RowPlan *p) {
+    const int es = (int)dtype_size(dt);
+    p->vec = vec_ok ? 16 / es : 1;
+    const int64_t nv = N / p->vec;
+    const int *its = vec_ok ? kVecIts : kScalarIts;
+    const int n_its = vec_ok ? 6 : 7;
+    int best_tpr = -1, best_it = -1;
+    int64_t best_waste = INT64_MAX;
+    // Smallest idle-slot count; ties go to more vectors per thread (fewer,
+    // longer-running threads keep more loads in flight per thread).
+    for (int tpr = 1; tpr <= 1024; tpr *= 2) {
+        for (int i = 0; i < n_its; ++i) {
+            const int it = its[i];
+            if ((int64_t)tpr * it < nv) continue;
+            const int64_t waste = (int64_t)tpr * it - nv;
+            if (waste < best_waste || (waste == best_waste && it > best_it)) {
+                best_waste = waste; best_tpr = tpr; best_it = it;
+            }
+        }
+    }
+    if (best_tpr < 0) return false;
+    int bpc = backward ? 2 : 4;
+    int otpr, oit, obpc;
+    if (env_override(&otpr, &oit, &obpc) && otpr >= 1 && otpr <= 1024 && (otpr & (otpr - 1)) == 0 &&
+        (int64_t)otpr * oit >= nv && obpc >= 1 && obpc <= kMaxBwdBlocksPerCU) {
+        bool it_ok = false;
+        for (int i = 0; i < n_its; ++i) it_ok |= its[i] == oit;
+        if (it_ok) { best_tpr = otpr; best_it = oit; bpc = obpc; }
+    }
+    p->tpr = best_tpr;
+    p->it = best_it;
+    p->block = best_tpr >= 256 ? best_tpr : 256;
+    const int rpb = p->block / p->tpr;
+    const int64_t needed = ceil_div(M, rpb);
+    const int64_t cap = (int64_t)device_cu_count() * bpc;
+    p->grid = (int)(needed < cap ? needed : cap);
+    if (p->grid < 1) p->grid = 1;
+    return true;
+}
+
+// The backward grid (= number of partial rows) never exceeds
+// CUs * kMaxBwdBlocksPerCU nor M, so that bounds the workspace.
+static int64_t max_partial_rows(int64_t M) {
+    const int64_t cap = (int64_t)device_cu_count() * kMaxBwdBlocksPerCU;
+    return M < cap ? (M > 0 ? M : 1) : cap;
+}
+
+// -------------------------------------------------------------- dispatch
+template <typename T, bool RMS, int V>
+static norm_status launch_fwd_v(const RowPlan &p, hipStream_t s, const void *x, const void *w,
+                                const void *b, void *y, float *mean, float *rstd, int64_t M,
+                                int N, float eps) {
+    using fn_t = void (*)(const T *, const T *, const T *, T *, float *, float *, int64_t, int,
+                          float, float, int);
+    fn_t fn = nullptr;
+    switch (p.it) {
+    case 1: fn = p.block > 256 ? row_fwd_kernel<T, V, 1, RMS, 1024> : row_fwd_kernel<T, V, 1, RMS, 256>; break;
+    case 2: fn = p.block > 256 ? row_fwd_kernel<T, V, 2, RMS, 1024> : row_fwd_kernel<T, V, 2, RMS, 256>; break;
+    case 3: if constexpr (V > 1) fn = p.block > 256 ? row_fwd_kernel<T, V, 3, RMS, 1024> : row_fwd_kernel<T, V, 3, RMS, 256>; break;
+    case 4: fn = p.block > 256 ? row_fwd_kernel<T, V, 4, RMS, 1024> : row_fwd_kernel<T, V, 4, RMS, 256>; break;
+    case 6: if constexpr (V > 1) fn = p.block > 256 ? row_fwd_kernel<T, V, 6, RMS, 1024> : row_fwd_kernel<T, V, 6, RMS, 256>; break;
+    case 8: fn = p.block > 256 ? row_fwd_kernel<T, V, 8, RMS, 1024> : row_fwd_kernel<T, V, 8, RMS, 256>; break;
+    case 16: if constexpr (V == 1) fn = p.block > 256 ? row_fwd_kernel<T, V, 16, RMS, 1024> : row_fwd_kernel<T, V, 16, RMS, 256>; break;
+    case 32: if constexpr (V == 1) fn = p.block > 256 ? row_fwd_kernel<T, V, 32, RMS, 1024> : row_fwd_kernel<T, V, 32, RMS, 256>; break;
+    case 64: if constexpr (V == 1) fn = p.block > 256 ? row_fwd_kernel<T, V, 64, RMS, 1024> : row_fwd_kernel<T, V, 64, RMS, 256>; break;
+    }
+    if (!fn) return NORM_ERR_SHAPE;
+    hook_before(s, RMS ? "row_fwd_kernel<rms>" : "row_fwd_kernel<ln>");
+    hipLaunchKernelGGL(fn, dim3(p.grid), dim3(p.block), 0, s, (const T *)x, (const T *)w,
+                       (const T *)b, (T *)y, mean, rstd, M, N, 1.0f / (float)N, eps, p.tpr);
+    hook_after(s);
+    return launch_status();
+}
+
+template <typename T, bool RMS, int V>
+static norm_status launch_bwd_v(const RowPlan &p, hipStream_t s, const void *dy, const void *x,
+                                const void *w, const float *mean, const float *rstd, void *dx,
+                                float *part_w, float *part_b, int64_t M, int N) {
+    using fn_t = void (*)(const T *, const T *, const T *, const float *, const float *, T *,
+                          float *, float *, int64_t, int, float, int);
+    fn_t fn = nullptr;
+    switch (p.it) {
+    case 1: fn = p.block > 256 ? row_bwd_kernel<T, V, 1, RMS, 1024> : row_bwd_kernel<T, V, 1, RMS, 256>; break;
+    case 2: fn = p.block > 256 ? row_bwd_kernel<T, V, 2, RMS, 1024> : row_bwd_kernel<T, V, 2, RMS, 256>; break;
+    case 3: if constexpr (V > 1) fn = p.block > 256 ? row_bwd_kernel<T, V, 3, RMS, 1024> : row_bwd_kernel<T, V, 3, RMS, 256>; break;
+    case 4: fn = p.block > 256 ? row_bwd_kernel<T, V, 4, RMS, 1024> : row_bwd_kernel<T, V, 4, RMS, 256>; break;
+    case 6: if constexpr (V > 1) fn = p.block > 256 ? row_bwd_kernel<T, V, 6, RMS, 1024> : row_bwd_kernel<T, V, 6, RMS, 256>; break;
+    case 8: fn = p.block > 256 ? row_bwd_kernel<T, V, 8, RMS, 1024> : row_bwd_kernel<T, V, 8, RMS, 256>; break;
+    case 16: if constexpr (V == 1) fn = p.block > 256 ? row_bwd_kernel<T, V, 16, RMS, 1024> : row_bwd_kernel<T, V, 16, RMS, 256>; break;
+    case 32: if constexpr (V == 1) fn = p.block > 256 ? row_bwd_kernel<T, V, 32, RMS, 1024> : row_bwd_kernel<T, V, 32, RMS, 256>; break;
+    case 64: if constexpr (V == 1) fn = p.block > 256 ? row_bwd_kernel<T, V, 64, RMS, 1024> : row_bwd_kernel<T, V, 64, RMS, 256>; break;
+    }
+    if (!fn) return NORM_ERR_SHAPE;
+    const size_t shmem = (part_w || part_b) ? (size_t)p.block * V * sizeof(float) : 0;
+    hook_before(s, RMS ? "row_bwd_kernel<rms>" : "row_bwd_kernel<ln>");
+    hipLaunchKernelGGL(fn, dim3(p.grid), dim3(p.block), shmem, s, (const T *)dy, (const T *)x,
+                       (const T *)w, mean, rstd, (T *)dx, part_w, part_b, M, N,
+                       1.0f / (float)N, p.tpr);
+    hook_after(s);
+    return launch_status();
+}
+
+static bool row_vec_ok(norm_dtype dt, int64_t N, std::initializer_list<const void *> ptrs) {
+    if ((N * (int64_t)dtype_size(dt)) % 16 != 0) return false;
+    for (const void *q : ptrs)
+        if (q && !aligned16(q)) return false;
+    return true;
+}
+
+static norm_status check_rows(norm_dtype dt, int64_t M, int64_t N) {
+    if (!dtype_ok(dt)) return NORM_ERR_DTYPE;
+    if (M < 0 || N < 1) return NORM_ERR_SHAPE;
+    if (N > (dt == NORM_BF16 ? NORM_MAX_N_BF16 : NORM_MAX_N_F32)) return NORM_ERR_SHAPE;
+    if (M > (int64_t)1 << 40) return NORM_ERR_SHAPE;
+    return NORM_OK;
+}
+
+template <bool RMS>
+static norm_status fwd_entry(norm_dtype dt, int64_t M, int64_t N, float eps, const void *x,
+                             const void *w, const void *b, void *y, float *mean, float *rstd,
+                             void *stream) {
+    norm_status st = check_rows(dt, M, N);
+    if (st != NORM_OK) return st;
+    if (!(eps >= 0.0f)) return NORM_ERR_ARG;
+    if (M == 0) return NORM_OK;
+    if (!x || !y) return NORM_ERR_NULL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool vec = row_vec_ok(dt, N, {x, w, b, y});
+    RowPlan p;
+    if (!make_plan(dt, M, N, vec, false, &p)) return NORM_ERR_SHAPE;
+    const int n = (int)N;
+    if (dt == NORM_F32)
+        return vec ? launch_fwd_v<float, RMS, 4>(p, s, x, w, b, y, mean, rstd, M, n, eps)
+                   : launch_fwd_v<float, RMS, 1>(p, s, x, w, b, y, mean, rstd, M, n, eps);
+    return vec ? launch_fwd_v<bf16_t, RMS, 8>(p, s, x, w, b, y, mean, rstd, M, n, eps)
+               : launch_fwd_v<bf16_t, RMS, 1>(p, s, x, w, b, y, mean, rstd, M, n, eps);
+}
+
+static size_t bwd_ws_bytes(norm_dtype dt, int64_t M, int64_t N, int nparts) {
+    if (check_rows(dt, M, N) != NORM_OK) return 0;
+    return (size_t)max_partial_rows(M) * (size_t)N * sizeof(float) * (size_t)nparts;
+}
+
+template <bool RMS>
+static norm_status bwd_entry(norm_dtype dt, int64_t M, int64_t N, const void *dy, const void *x,
+                             const void *w, const float *mean, const float *rstd, void *dx,
+                             void *dw, void *db, void *ws, size_t ws_bytes, void *stream) {
+    norm_status st = check_rows(dt, M, N);
+    if (st != NORM_OK) return st;
+    if (!dy || !x || !rstd || !dx || (!RMS && !mean)) {
+        if (M == 0 && !(dw || db)) return NORM_OK;
+        if (M > 0) return NORM_ERR_NULL;
+    }
+    const bool want = dw || db;
+    const size_t need = want ? bwd_ws_bytes(dt, M, N, RMS ? 1 : 2) : 0;
+    if (want && (ws == nullptr || ws_bytes < need)) return NORM_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int n = (int)N;
+    if (M == 0) {
+        // Empty batch: the parameter gradients are sums over no rows.
+        if (!want) return NORM_OK;
+        const dim3 grid((unsigned)ceil_div(N, 256));
+        for (void *out : {dw, db}) {
+            if (!out) continue;
+            if (dt == NORM_F32)
+                hipLaunchKernelGGL(zero_fill_kernel<float>, grid, dim3(256), 0, s, (float *)out, n);
+            else
+                hipLaunchKernelGGL(zero_fill_kernel<bf16_t>, grid, dim3(256), 0, s, (bf16_t *)out, n);
+        }
+        return launch_status();
+    }
+    const bool vec = row_vec_ok(dt, N, {dy, x, w, dx});
+    RowPlan p;
+    if (!make_plan(dt, M, N, vec, true, &p)) return NORM_ERR_SHAPE;
+    float *part_w = dw ? static_cast<float *>(ws) : nullptr;
+    float *part_b = (!RMS && db) ? static_cast<float *>(ws) + (size_t)max_partial_rows(M) * N : nullptr;
+    if (dt == NORM_F32)
+        st = vec ? launch_bwd_v<float, RMS, 4>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n)
+                 : launch_bwd_v<float, RMS, 1>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n);
+    else
+        st = vec ? launch_bwd_v<bf16_t, RMS, 8>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n)
+                 : launch_bwd_v<bf16_t, RMS, 1>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n);
+    if (st != NORM_OK || !want) return st;
+    dim3 grid((unsigned)ceil_div(N, 64), RMS ? 1 : 2);
+    if (dt == NORM_F32)
+        hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(64, 4), 0, s, part_w, part_b, p.grid, n,
+                           (float *)dw, (float *)db);
+    else
+        hipLaunchKernelGGL(colsum_kernel<bf16_t>, grid, dim3(64, 4), 0, s, part_w, part_b, p.grid, n,
+                           (bf16_t *)dw, (bf16_t *)db);
+    return launch_status();
+}
+
+}  // namespace mi355norm
+
+using namespace mi355norm;
+
+extern "C" norm_status ln_fwd(norm_dtype dt, int64_t M, int64_t N, float eps, const void *x,
+                              const void *w, const void *b, void *y, float *mean, float *rstd,
+                              void *stream) {
+    return fwd_entry<false>(dt, M, N, eps, x, w, b, y, mean, rstd, stream);
+}
+
+extern "C" size_t ln_bwd_workspace_bytes(norm_dtype dt, int64_t M, int64_t N) {
+    return bwd_ws_bytes(dt, M, N, 2);
+}
+
+extern "C" norm_status ln_bwd(norm_dtype dt, int64_t M, int64_t N, const void *dy, const void *x,
+                              const void *w, const float *mean, const float *rstd, void *dx,
+                              void *dw, void *db, void *ws, size_t ws_bytes, void *stream) {
+    return bwd_entry<false>(dt, M, N, dy, x, w, mean, rstd, dx, dw, db, ws, ws_bytes, stream);
+}
+
+extern "C" norm_status rms_fwd(norm_dtype dt, int64_t M, int64_t N, float eps, const void *x,
+                               const void *w, void *y, float *rstd, void *stream) {
+    return fwd_entry<true>(dt, M, N, eps, x, w, nullptr, y, nullptr, rstd, stream);
+}
+
+extern "C" size_t rms_bwd_workspace_bytes(norm_dtype dt, int64_t M, int64_t N) {
+    return bwd_ws_bytes(dt, M, N, 1);
+}
+
+extern "C" norm_status rms_bwd(norm_dtype dt, int64_t M, int64_t N, const void *dy, const void *x,
+                               const void *w, const float *rstd, void *dx, void *dw, void *ws,
+                               size_t ws_bytes, void *stream) {
+    return bwd_entry<true>(dt, M, N, dy, x, w, nullptr, rstd, dx, dw, nullptr, ws, ws_bytes, stream);
+}

@@ -1,0 +1,134 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/mi355norm.h declares, and rejects bad arguments on the host (the
+validation runs before anything touches the HIP runtime)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi355norm.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EACT, EARG, EWS = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+P = ctypes.c_void_p(4096)  # a non-NULL pointer that validation must reject before use
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from normalization_ln_rmsnorm_amd import normlib
+    if not os.path.exists(normlib.LIB_PATH):
+        from normalization_ln_rmsnorm_amd import build
+        build.build()
+    return normlib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["ln_fwd", "ln_bwd", "ln_bwd_workspace_bytes", "rms_fwd", "rms_bwd",
+              "rms_bwd_workspace_bytes", "bn_workspace_bytes", "bn_fwd_train", "bn_fwd_eval",
+              "bn_bwd", "norm_status_str", "norm_arm_kernel_events", "norm_last_kernel_name"]:
+        assert n in names, n
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from normalization_ln_rmsnorm_amd import normlib
+    out = subprocess.run(["nm", "-D", "--defined-only", normlib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in declared_functions():
+        assert n in exported, f"{n} declared in mi355norm.h but not exported"
+        getattr(lib, n)
+
+
+def test_status_strings(lib):
+    for code in (OK, ENULL, ESHAPE, EDTYPE, EACT, EARG, EWS, -7, 99):
+        s = lib.norm_status_str(code)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+def test_row_errors(lib):
+    # dtype, shapes, eps, null pointers
+    assert lib.ln_fwd(7, 4, 8, 1e-5, P, NULL, NULL, P, NULL, NULL, NULL) == EDTYPE
+    assert lib.ln_fwd(F32, 4, 0, 1e-5, P, NULL, NULL, P, NULL, NULL, NULL) == ESHAPE
+    assert lib.ln_fwd(F32, -1, 8, 1e-5, P, NULL, NULL, P, NULL, NULL, NULL) == ESHAPE
+    assert lib.ln_fwd(F32, 4, 32769, 1e-5, P, NULL, NULL, P, NULL, NULL, NULL) == ESHAPE
+    assert lib.ln_fwd(BF16, 4, 65537, 1e-5, P, NULL, NULL, P, NULL, NULL, NULL) == ESHAPE
+    assert lib.ln_fwd(F32, 4, 8, -1.0, P, NULL, NULL, P, NULL, NULL, NULL) == EARG
+    assert lib.ln_fwd(F32, 4, 8, float("nan"), P, NULL, NULL, P, NULL, NULL, NULL) == EARG
+    assert lib.ln_fwd(F32, 4, 8, 1e-5, NULL, NULL, NULL, P, NULL, NULL, NULL) == ENULL
+    assert lib.ln_fwd(F32, 4, 8, 1e-5, P, NULL, NULL, NULL, NULL, NULL, NULL) == ENULL
+    assert lib.ln_fwd(F32, 0, 8, 1e-5, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == OK
+    assert lib.rms_fwd(F32, 4, 8, 1e-5, NULL, NULL, P, NULL, NULL) == ENULL
+    assert lib.rms_fwd(BF16, 4, 8, -2.0, P, NULL, P, NULL, NULL) == EARG
+    # backward: missing statistics, workspace
+    assert lib.ln_bwd(F32, 4, 8, P, P, NULL, NULL, P, P, NULL, NULL, NULL, 0, NULL) == ENULL
+    assert lib.ln_bwd(F32, 4, 8, P, P, NULL, P, NULL, P, NULL, NULL, NULL, 0, NULL) == ENULL
+    need = lib.ln_bwd_workspace_bytes(F32, 4, 8)
+    assert need >= 4 * 8 * 4
+    assert lib.ln_bwd(F32, 4, 8, P, P, NULL, P, P, P, P, NULL, NULL, 0, NULL) == EWS
+    assert lib.ln_bwd(F32, 4, 8, P, P, NULL, P, P, P, P, NULL, P, need - 1, NULL) == EWS
+    assert lib.rms_bwd(F32, 4, 8, P, P, NULL, NULL, P, NULL, NULL, 0, NULL) == ENULL
+    assert lib.rms_bwd(F32, 4, 8, P, P, NULL, P, P, P, NULL, 0, NULL) == EWS
+    assert lib.rms_bwd_workspace_bytes(F32, 4, 8) >= 4 * 8 * 4
+    assert lib.ln_bwd_workspace_bytes(9, 4, 8) == 0
+    assert lib.rms_bwd_workspace_bytes(F32, 4, 0) == 0
+
+
+def test_bn_errors(lib):
+    ws = lib.bn_workspace_bytes(F32, 2, 3, 5)
+    assert ws > 0
+    args = lambda **k: dict(dict(dt=F32, Nb=2, C=3, HW=5, eps=1e-5, mom=0.1, act=0, x=P, res=NULL,
+                                 w=NULL, b=NULL, rm=NULL, rv=NULL, sm=P, sr=P, y=P, ws=P,
+                                 wsb=ws, s=NULL), **k)
+
+    def train(**k):
+        a = args(**k)
+        return lib.bn_fwd_train(a["dt"], a["Nb"], a["C"], a["HW"], a["eps"], a["mom"], a["act"],
+                                a["x"], a["res"], a["w"], a["b"], a["rm"], a["rv"], a["sm"],
+                                a["sr"], a["y"], a["ws"], a["wsb"], a["s"])
+
+    assert train(dt=4) == EDTYPE
+    assert train(act=3) == EACT
+    assert train(act=-1) == EACT
+    assert train(mom=1.5) == EARG
+    assert train(mom=-0.1) == EARG
+    assert train(eps=-1.0) == EARG
+    assert train(Nb=1, HW=1) == EARG        # one value per channel: no unbiased variance
+    assert train(Nb=-1) == ESHAPE
+    assert train(x=NULL) == ENULL
+    assert train(sm=NULL) == ENULL
+    assert train(y=NULL) == ENULL
+    assert train(ws=NULL) == EWS
+    assert train(wsb=ws - 1) == EWS
+    assert train(C=0) == OK
+    assert lib.bn_fwd_eval(F32, 2, 3, 5, 1e-5, 0, P, NULL, NULL, NULL, NULL, P, P, NULL) == ENULL
+    assert lib.bn_fwd_eval(F32, 2, 3, 5, 1e-5, 5, P, NULL, NULL, NULL, P, P, P, NULL) == EACT
+    assert lib.bn_fwd_eval(F32, 0, 3, 5, 1e-5, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == OK
+    # backward: residual without dres, missing saved statistics, workspace
+    assert lib.bn_bwd(F32, 2, 3, 5, 0, P, P, P, NULL, NULL, P, P, P, NULL, NULL, NULL, P, ws,
+                      NULL) == ENULL
+    assert lib.bn_bwd(F32, 2, 3, 5, 0, P, P, NULL, NULL, NULL, NULL, P, P, NULL, NULL, NULL, P, ws,
+                      NULL) == ENULL
+    assert lib.bn_bwd(F32, 2, 3, 5, 0, P, P, NULL, NULL, NULL, P, P, P, NULL, NULL, NULL, P, 8,
+                      NULL) == EWS
+    assert lib.bn_bwd(F32, 2, 3, 5, 7, P, P, NULL, NULL, NULL, P, P, P, NULL, NULL, NULL, P, ws,
+                      NULL) == EACT
+    assert lib.bn_workspace_bytes(F32, -1, 3, 5) == 0
+
+
+def test_workspace_sizes_scale(lib):
+    small = lib.bn_workspace_bytes(F32, 64, 256, 3136)
+    big = lib.bn_workspace_bytes(BF16, 256, 64, 12544)
+    assert 0 < small < 1 << 22 and 0 < big < 1 << 22
+    assert lib.rms_bwd_workspace_bytes(BF16, 16384, 4096) <= 64 << 20

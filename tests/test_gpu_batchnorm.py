@@ -1,0 +1,129 @@
+"""GPU parity: BatchNorm training forward, eval forward and backward (with
+the fused residual and ReLU / exact-GELU activation) through the C ABI
+against the float64 oracle, element by element.
+
+ReLU cases move the inputs off the kink of the derivative first
+(tests._parity.avoid_relu_kink): at z = 0 either gradient is valid.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from tests._parity import avoid_relu_kink, check, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+nl = pytest.importorskip("normalization_ln_rmsnorm_amd")
+from normalization_ln_rmsnorm_amd.workloads import WORKLOADS, gen_bn  # noqa: E402
+
+
+def _wl(dtype, act, residual):
+    base = WORKLOADS["bn_f32_64x256x56x56"] if dtype == "f32" else WORKLOADS["bn_bf16_256x64x112x112"]
+    return dataclasses.replace(base, act=act, residual=residual)
+
+
+def run_case(orc, dtype, Nb, C, HW, act, residual, with_wb=True, eval_after=True, report=None,
+             inp=None, wl=None):
+    wl = wl or _wl(dtype, act, residual)
+    if inp is None:
+        inp = gen_bn(wl, Nb=Nb, C=C, HW=HW)
+    bf16 = dtype == "bf16"
+    eps, mom = wl.eps, wl.momentum
+    if act == "relu":
+        inp, moved = avoid_relu_kink(orc, inp, dtype, eps)
+    shape = (Nb, C, HW)
+    x = to_dev(inp["x"], dtype)
+    res = to_dev(inp["res"], dtype) if residual else None
+    w = to_dev(inp["w"], dtype) if with_wb else None
+    b = to_dev(inp["b"], dtype) if with_wb else None
+    dy = to_dev(inp["dy"], dtype)
+    rm = torch.from_numpy(inp["running_mean"].copy()).cuda()
+    rv = torch.from_numpy(inp["running_var"].copy()).cuda()
+    w_np = inp["w"] if with_wb else None
+    b_np = inp["b"] if with_wb else None
+    res_np = inp["res"] if residual else None
+
+    y, sm, sr = nl.bn_fwd_train(x, w, b, rm, rv, eps, mom, act, res)
+    dx, dres, dw, db = nl.bn_bwd(dy, x, w, b, sm, sr, act, res, want_dw=with_wb, want_db=with_wb)
+    ye = nl.bn_fwd_eval(x, w, b, rm, rv, eps, act, res) if eval_after else None
+    torch.cuda.synchronize()
+
+    ry, rsm, rsr, rrm, rrv = orc.bn_fwd_train(inp["x"], res_np, w_np, b_np, inp["running_mean"],
+                                              inp["running_var"], eps=eps, momentum=mom, act=act,
+                                              bf16=bf16)
+    rdx, rdres, rdw, rdb = orc.bn_bwd(inp["dy"], inp["x"], res_np, w_np, b_np, eps=eps, act=act,
+                                      bf16=bf16)
+    tag = f"bn/{dtype}/{Nb}x{C}x{HW}/{act}/res={residual}"
+    ch = (0, 2)  # bf16 floor taken per channel
+    check(f"{tag} y", to_f64(y), ry, dtype, group_axis=ch, report=report)
+    check(f"{tag} save_mean", to_f64(sm), rsm, "f32", report=report)
+    check(f"{tag} save_rstd", to_f64(sr), rsr, "f32", report=report)
+    check(f"{tag} running_mean", to_f64(rm), rrm, "f32", report=report)
+    check(f"{tag} running_var", to_f64(rv), rrv, "f32", report=report)
+    # Scale of the terms dx is formed from: |w_c * rstd_c| * max |dy| per channel.
+    wabs = np.abs(orc.widen(w_np, bf16=bf16)) if with_wb else np.ones(C)
+    dymax = np.abs(orc.widen(inp["dy"], bf16=bf16)).max(axis=(0, 2))
+    dx_scale = (wabs * rsr * dymax)[None, :, None]
+    check(f"{tag} dx", to_f64(dx), rdx, dtype, group_axis=ch, report=report, scale=dx_scale)
+    if residual:
+        check(f"{tag} dres", to_f64(dres), rdres, dtype, group_axis=ch, report=report)
+    if with_wb:
+        check(f"{tag} dw", to_f64(dw), rdw, dtype, report=report)
+        check(f"{tag} db", to_f64(db), rdb, dtype, report=report)
+    if eval_after:
+        # Eval reads the running statistics the training step just wrote
+        # (float32 on the device, passed to the oracle as they stand).
+        rye = orc.bn_fwd_eval(inp["x"], to_f64(rm), to_f64(rv), res_np, w_np, b_np, eps=eps,
+                              act=act, bf16=bf16)
+        check(f"{tag} y_eval", to_f64(ye), rye, dtype, group_axis=ch, report=report)
+
+
+SMALL = [(2, 3, 5), (4, 8, 49), (3, 5, 1), (2, 4, 7), (5, 16, 64), (2, 2, 3136), (7, 3, 1000),
+         (1, 2, 12544), (16, 4, 24)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("act,residual", [("none", False), ("relu", True), ("gelu", False),
+                                          ("gelu", True), ("relu", False), ("none", True)])
+@pytest.mark.parametrize("Nb,C,HW", SMALL)
+def test_small_shapes(orc, dtype, act, residual, Nb, C, HW):
+    print(f"case bn {dtype} {Nb}x{C}x{HW} {act} res={residual}", flush=True)
+    run_case(orc, dtype, Nb, C, HW, act, residual)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_no_affine(orc, dtype):
+    run_case(orc, dtype, 4, 6, 50, "gelu", True, with_wb=False)
+
+
+def test_two_values_pin_unbiased_running_var(orc):
+    """n = 2 per channel: the unbiased factor is 2, visible at any tolerance."""
+    run_case(orc, "f32", 2, 5, 1, "none", False)
+
+
+@pytest.mark.parametrize("name", ["bn_f32_64x256x56x56", "bn_bf16_256x64x112x112"])
+def test_full_size_workloads(orc, name):
+    wl = WORKLOADS[name]
+    Nb, C, H, W = wl.shape
+    print(f"case {name}", flush=True)
+    report = []
+    run_case(orc, wl.dtype, Nb, C, H * W, wl.act, wl.residual, eval_after=True, report=report,
+             wl=wl)
+    for r in report:
+        print(r, flush=True)
+
+
+def test_backward_bitwise_deterministic(orc):
+    wl = _wl("f32", "relu", True)
+    inp = gen_bn(wl, Nb=8, C=32, HW=784)
+    x, res, w, b, dy = (to_dev(inp[k], "f32") for k in ("x", "res", "w", "b", "dy"))
+    outs = []
+    for _ in range(2):
+        rm = torch.zeros(32, device="cuda"); rv = torch.ones(32, device="cuda")
+        y, sm, sr = nl.bn_fwd_train(x, w, b, rm, rv, wl.eps, wl.momentum, "relu", res)
+        outs.append((y, sm, sr) + nl.bn_bwd(dy, x, w, b, sm, sr, "relu", res))
+    torch.cuda.synchronize()
+    for a, b_ in zip(outs[0], outs[1]):
+        assert torch.equal(a, b_)

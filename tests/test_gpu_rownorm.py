@@ -1,0 +1,176 @@
+"""GPU parity: LayerNorm / RMSNorm forward and backward through the C ABI
+against the float64 oracle, element by element.
+
+Shapes span every tiling the planner picks (thread groups of 1..1024 lanes,
+vector and scalar paths, ragged tails) plus the four row-wise workloads at
+full size, launched exactly as the benchmark launches them.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from tests._parity import check, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+nl = pytest.importorskip("normalization_ln_rmsnorm_amd")
+from normalization_ln_rmsnorm_amd.workloads import WORKLOADS, gen_rowwise  # noqa: E402
+
+SENTINEL = float("nan")
+PAD = 64
+
+
+def _guarded(shape, dtype):
+    n = int(np.prod(shape))
+    buf = torch.full((n + 2 * PAD,), SENTINEL, dtype=dtype, device="cuda")
+    return buf, buf[PAD:PAD + n].view(*shape)
+
+
+def _guard_ok(buf, n):
+    head, tail = buf[:PAD], buf[PAD + n:]
+    return bool(torch.isnan(head.float()).all() and torch.isnan(tail.float()).all())
+
+
+def _wl(kind, dtype):
+    """The workload whose value recipe a small case borrows."""
+    if kind == "rms":
+        return dataclasses.replace(WORKLOADS["rms_bf16_16384x4096"], dtype=dtype)
+    return WORKLOADS["ln_bf16_25216x768"] if dtype == "bf16" else WORKLOADS["ln_f32_64x256"]
+
+
+def run_case(orc, kind, dtype, M, N, with_w=True, with_b=True, eps=None, seed=None, guard=True,
+             report=None):
+    wl = _wl(kind, dtype)
+    eps = wl.eps if eps is None else eps
+    inp = gen_rowwise(wl, M=M, N=N, seed=seed)
+    bf16 = dtype == "bf16"
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    x = to_dev(inp["x"], dtype)
+    dy = to_dev(inp["dy"], dtype)
+    w = to_dev(inp["w"], dtype) if with_w else None
+    b = to_dev(inp["b"], dtype) if (with_b and kind == "ln") else None
+    w_np = inp["w"] if with_w else None
+    b_np = inp["b"] if (with_b and kind == "ln") else None
+
+    ybuf, y = _guarded((M, N), tdt) if guard else (None, torch.empty(M, N, dtype=tdt, device="cuda"))
+    dxbuf, dx = _guarded((M, N), tdt) if guard else (None, torch.empty(M, N, dtype=tdt, device="cuda"))
+    if kind == "ln":
+        _, mean, rstd = nl.ln_fwd(x, w, b, eps, y=y)
+        dx_, dw, db = nl.ln_bwd(dy, x, w, mean, rstd, dx=dx, want_dw=with_w, want_db=with_b)
+        ry, rmean, rrstd = orc.ln_fwd(inp["x"], w_np, b_np, eps=eps, bf16=bf16)
+        rdx, rdw, rdb = orc.ln_bwd(inp["dy"], inp["x"], w_np, eps=eps, bf16=bf16)
+    else:
+        _, rstd = nl.rms_fwd(x, w, eps, y=y)
+        dx_, dw = nl.rms_bwd(dy, x, w, rstd, dx=dx, want_dw=with_w)
+        db = None
+        ry, rrstd = orc.rms_fwd(inp["x"], w_np, eps=eps, bf16=bf16)
+        rdx, rdw = orc.rms_bwd(inp["dy"], inp["x"], w_np, eps=eps, bf16=bf16)
+    torch.cuda.synchronize()
+    if guard:
+        assert _guard_ok(ybuf, M * N), "y: write outside the output"
+        assert _guard_ok(dxbuf, M * N), "dx: write outside the output"
+    tag = f"{kind}/{dtype}/{M}x{N}"
+    check(f"{tag} y", to_f64(y), ry, dtype, group_axis=1, report=report)
+    check(f"{tag} rstd", to_f64(rstd), rrstd, "f32", report=report)
+    if kind == "ln":
+        check(f"{tag} mean", to_f64(mean), rmean, "f32", report=report)
+    # Scale of the terms dx is formed from: rstd * |dy * w| per row.
+    g = np.abs(orc.widen(inp["dy"], bf16=bf16) * (orc.widen(w_np, bf16=bf16) if with_w else 1.0))
+    dx_scale = rrstd[:, None] * g.max(axis=1, keepdims=True)
+    check(f"{tag} dx", to_f64(dx), rdx, dtype, group_axis=1, report=report, scale=dx_scale)
+    if with_w:
+        check(f"{tag} dw", to_f64(dw), rdw, dtype, report=report)
+    if kind == "ln" and with_b:
+        check(f"{tag} db", to_f64(db), rdb, dtype, report=report)
+    return dict(x=x, dy=dy, w=w, b=b, mean=mean if kind == "ln" else None, rstd=rstd, dx=dx, dw=dw, db=db)
+
+
+SHAPES = [(1, 1), (3, 7), (64, 256), (37, 768), (33, 1000), (5, 1024), (130, 96), (300, 520),
+          (17, 4096), (3, 16384), (9, 3000), (2, 24)]
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N", SHAPES)
+def test_small_shapes(orc, kind, dtype, M, N):
+    print(f"case {kind} {dtype} {M}x{N}", flush=True)
+    run_case(orc, kind, dtype, M, N)
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_widest_rows(orc, kind, dtype):
+    N = 65536 if dtype == "bf16" else 32768
+    print(f"case {kind} {dtype} 3x{N}", flush=True)
+    run_case(orc, kind, dtype, 3, N)
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+@pytest.mark.parametrize("with_w,with_b", [(False, False), (True, False), (False, True)])
+def test_optional_params(orc, kind, with_w, with_b):
+    print(f"case {kind} w={with_w} b={with_b}", flush=True)
+    run_case(orc, kind, "bf16", 19, 768, with_w=with_w, with_b=with_b)
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+def test_unaligned_scalar_path(orc, kind):
+    """Tensors that are not 16-byte aligned take the scalar path."""
+    M, N = 11, 96
+    wl = _wl(kind, "f32")
+    inp = gen_rowwise(wl, M=M, N=N)
+    big = torch.empty(M * N + 1, dtype=torch.float32, device="cuda")
+    x = big[1:].view(M, N)
+    x.copy_(to_dev(inp["x"], "f32"))
+    w = to_dev(inp["w"], "f32")
+    if kind == "ln":
+        y, mean, rstd = nl.ln_fwd(x, w, to_dev(inp["b"], "f32"), wl.eps)
+        ry, _, _ = orc.ln_fwd(inp["x"], inp["w"], inp["b"], eps=wl.eps)
+    else:
+        y, rstd = nl.rms_fwd(x, w, wl.eps)
+        ry, _ = orc.rms_fwd(inp["x"], inp["w"], eps=wl.eps)
+    check(f"{kind} unaligned y", to_f64(y), ry, "f32")
+
+
+@pytest.mark.parametrize("name", ["ln_f32_64x256", "rms_bf16_16384x4096", "ln_bf16_25216x768",
+                                  "ln_bf16_4096x1000"])
+def test_full_size_workloads(orc, name):
+    """The workloads at the sizes and launch configuration the benchmark uses."""
+    wl = WORKLOADS[name]
+    M, N = wl.shape
+    print(f"case {name}", flush=True)
+    report = []
+    run_case(orc, wl.kind, wl.dtype, M, N, guard=True, report=report)
+    for r in report:
+        print(r, flush=True)
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+def test_backward_bitwise_deterministic(orc, kind):
+    M, N = 2048, 4096
+    wl = _wl(kind, "bf16")
+    inp = gen_rowwise(wl, M=M, N=N)
+    x, dy, w = (to_dev(inp[k], "bf16") for k in ("x", "dy", "w"))
+    outs = []
+    for _ in range(2):
+        if kind == "ln":
+            b = to_dev(inp["b"], "bf16")
+            _, mean, rstd = nl.ln_fwd(x, w, b, wl.eps)
+            outs.append(nl.ln_bwd(dy, x, w, mean, rstd))
+        else:
+            _, rstd = nl.rms_fwd(x, w, wl.eps)
+            outs.append(nl.rms_bwd(dy, x, w, rstd))
+    torch.cuda.synchronize()
+    for a, b in zip(outs[0], outs[1]):
+        if a is not None:
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_empty_batch_is_noop(orc):
+    x = torch.empty(0, 64, device="cuda")
+    y, mean, rstd = nl.ln_fwd(x, None, None, 1e-5)
+    assert y.shape == (0, 64)
+    dx, dw, db = nl.ln_bwd(x, x, torch.ones(64, device="cuda"), mean, rstd)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 0) and torch.all(db == 0)
