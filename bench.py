@@ -8,9 +8,12 @@ workloads: training forward, backward, and the eval forward when the workload
 has one) on seeded synthetic inputs already resident in HBM.  Before every
 operation a 512 MiB scratch buffer is written, so inputs come from HBM rather
 than the 256 MB Infinity Cache; that flush is outside the timed spans.  Each
-operation is timed with HIP events on the stream its kernels run on; the
-main streaming kernel of the dominant operation is also bracketed by its own
-pair of HIP events through the library's timing hook.
+operation is timed on the device: the library attaches caller-created HIP
+events to its kernels' own dispatches (norm_arm_kernel_events), so an
+operation's time runs from its first kernel's start to its last kernel's end
+and the main streaming kernel's duration is measured by itself -- the same
+quantities rocprofv3's kernel trace reports.  Host-side events around each
+call are recorded too (they add the ~6 us dispatch latency of a lone launch).
 
 Bytes are algorithmic: what the method must move (every activation tensor in
 its I/O dtype once per pass that touches it, plus the small vectors), not
@@ -98,10 +101,10 @@ def bytes_bn(wl, es):
     fwd_kernel = (1 + res + 1) * U           # the apply kernel alone
     if res:
         bwd = 7 * U + small                  # pass 1: dy, x, res -> dres; pass 2: dres, x -> dx
-        bwd_kernel = 3 * U
+        bwd_kernel = 4 * U                   # main kernel: pass 1
     else:
         bwd = 5 * U + small                  # pass 1: dy, x; pass 2: dy, x -> dx
-        bwd_kernel = 3 * U
+        bwd_kernel = 3 * U                   # main kernel: pass 2
     ev = (2 + res) * U + small if wl.eval_after_train else 0
     return dict(fwd=fwd, bwd=bwd, eval=ev, fwd_kernel=fwd_kernel, bwd_kernel=bwd_kernel)
 
@@ -197,22 +200,29 @@ class BnBench:
                            y=self.ye)
 
 
+MAX_KERNELS = 4  # kernels per operation timed through the library's hook
+
+
 def measure(bench, steps, warmup, torch, hip, nl, flush):
-    """Times every op of `steps` steps; returns per-op and dominant-kernel ms."""
+    """Runs `steps` timed steps.  Per operation it records (a) the device
+    span from its first kernel's start to its last kernel's end, via HIP
+    events the library attaches to the kernels' own dispatches, (b) the main
+    streaming kernel's own duration the same way, and (c) host-side events
+    around the call (adds dispatch latency)."""
     def one_step(record):
         out = {}
         for op in bench.ops:
             flush.add_(1)
             if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                k0, k1 = (hip.event(), hip.event()) if op == bench.dominant else (None, None)
-                if k0 is not None:
-                    nl.arm_kernel_events(k0, k1)
-                e0.record()
+                evs = [hip.event() for _ in range(2 * MAX_KERNELS)]
+                nl.arm_kernel_events(evs)
+                h0 = torch.cuda.Event(enable_timing=True)
+                h1 = torch.cuda.Event(enable_timing=True)
+                h0.record()
                 bench.run(op)
-                e1.record()
-                out[op] = (e0, e1, k0, k1)
+                h1.record()
+                names, main = nl.last_kernels()
+                out[op] = (evs, names, main, h0, h1)
             else:
                 bench.run(op)
         return out
@@ -224,33 +234,52 @@ def measure(bench, steps, warmup, torch, hip, nl, flush):
     recs = [one_step(True) for _ in range(steps)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    op_ms = {op: [r[op][0].elapsed_time(r[op][1]) for r in recs] for op in bench.ops}
-    kern_ms = [hip.elapsed_ms(r[bench.dominant][2], r[bench.dominant][3]) for r in recs]
-    return op_ms, kern_ms, wall, nl.last_kernel_name()
+    dev_ms, host_ms, main_ms, kern_ms = {}, {}, {}, {}
+    names_main = {}
+    for op in bench.ops:
+        d, h, m = [], [], []
+        per_kernel = None
+        for r in recs:
+            evs, names, main, h0, h1 = r[op]
+            k = min(len(names), MAX_KERNELS)
+            d.append(hip.elapsed_ms(evs[0], evs[2 * k - 1]))
+            h.append(h0.elapsed_time(h1))
+            m.append(hip.elapsed_ms(evs[2 * main], evs[2 * main + 1]) if main >= 0 else float("nan"))
+            ks = [hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(k)]
+            per_kernel = [p + [t] for p, t in zip(per_kernel, ks)] if per_kernel else [[t] for t in ks]
+            names_main[op] = (names, main)
+        dev_ms[op], host_ms[op], main_ms[op] = d, h, m
+        kern_ms[op] = {f"{i}:{names_main[op][0][i]}": float(np.mean(v)) * 1e3
+                       for i, v in enumerate(per_kernel or [])}
+    return dict(dev=dev_ms, host=host_ms, main=main_ms, kernels_us=kern_ms, names=names_main,
+                wall=wall)
 
 
-def summarize(bench, op_ms, kern_ms, steps):
+def summarize(bench, meas):
     wl = bench.wl
     res = {"workload": wl.name, "rows": wl.rows}
     tot_bytes, tot_ms = 0, 0.0
     for op in bench.ops:
-        ms = float(np.mean(op_ms[op]))
+        dev = meas["dev"][op]
+        ms = float(np.mean(dev))
         b = bench.bytes[op]
-        res[op] = {"ms_mean": ms, "ms_p10": float(np.percentile(op_ms[op], 10)),
-                   "ms_p50": float(np.percentile(op_ms[op], 50)),
-                   "ms_p90": float(np.percentile(op_ms[op], 90)),
+        res[op] = {"ms_mean": ms, "ms_p10": float(np.percentile(dev, 10)),
+                   "ms_p50": float(np.percentile(dev, 50)),
+                   "ms_p90": float(np.percentile(dev, 90)),
+                   "ms_host_events_incl_launch": float(np.mean(meas["host"][op])),
                    "bytes": b, "GBps": b / ms / 1e6, "frac_of_peak": b / ms / 1e6 / PEAK_HBM_GBPS,
-                   "rows_per_s": wl.rows / (ms / 1e3)}
+                   "rows_per_s": wl.rows / (ms / 1e3), "kernels_us": meas["kernels_us"][op]}
         if op in ("fwd", "bwd"):
             tot_bytes += b
             tot_ms += ms
     res["fwd_bwd"] = {"ms": tot_ms, "bytes": tot_bytes, "GBps": tot_bytes / tot_ms / 1e6,
                       "frac_of_peak": tot_bytes / tot_ms / 1e6 / PEAK_HBM_GBPS,
                       "rows_per_s": wl.rows / (tot_ms / 1e3)}
-    km = float(np.mean(kern_ms))
+    names, main = meas["names"][bench.dominant]
+    km = float(np.mean(meas["main"][bench.dominant]))
     kb = bench.bytes[bench.dominant + "_kernel"]
-    res["dominant_kernel"] = {"op": bench.dominant, "avg_us": km * 1e3, "bytes": kb,
-                              "GBps": kb / km / 1e6}
+    res["dominant_kernel"] = {"op": bench.dominant, "kernel": names[main] if main >= 0 else "",
+                              "avg_us": km * 1e3, "bytes": kb, "GBps": kb / km / 1e6}
     return res
 
 
@@ -328,8 +357,9 @@ def main():
     wl = WORKLOADS[name]
     mk = RowBench if wl.kind in ("ln", "rms") else BnBench
     bench = mk(wl, nl, torch)
-    op_ms, kern_ms, wall, kname = measure(bench, args.steps, args.warmup, torch, hip, nl, flush)
-    head = summarize(bench, op_ms, kern_ms, args.steps)
+    meas = measure(bench, args.steps, args.warmup, torch, hip, nl, flush)
+    head = summarize(bench, meas)
+    wall = meas["wall"]
     print(f"[bench] {name}: fwd {head['fwd']['ms_mean']*1e3:.1f} us  bwd {head['bwd']['ms_mean']*1e3:.1f} us  "
           f"fwd+bwd {head['fwd_bwd']['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
 
@@ -340,8 +370,7 @@ def main():
                 continue
             ow = WORKLOADS[other]
             b = (RowBench if ow.kind in ("ln", "rms") else BnBench)(ow, nl, torch)
-            o_ms, k_ms, _, _ = measure(b, args.other_steps, 3, torch, hip, nl, flush)
-            per[other] = summarize(b, o_ms, k_ms, args.other_steps)
+            per[other] = summarize(b, measure(b, args.other_steps, 3, torch, hip, nl, flush))
             print(f"[bench] {other}: " + "  ".join(
                 f"{op} {per[other][op]['ms_mean']*1e3:.1f} us {per[other][op]['GBps']:.0f} GB/s"
                 for op in b.ops), file=sys.stderr, flush=True)
@@ -363,9 +392,9 @@ def main():
     del src, dst
 
     dk = head["dominant_kernel"]
-    traffic = load_traffic(f"{kname}|{name}")
+    traffic = load_traffic(f"{dk['kernel']}|{name}")
     roofline = {"bound": "hbm", "achieved": dk["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": dk["GBps"] / PEAK_HBM_GBPS, "traffic": traffic, "kernel": kname,
+                "frac": dk["GBps"] / PEAK_HBM_GBPS, "traffic": traffic, "kernel": dk["kernel"],
                 "bytes_per_launch": dk["bytes"], "avg_us": dk["avg_us"]}
     fb = head["fwd_bwd"]
     out = {
@@ -377,7 +406,7 @@ def main():
         "pct_of_peak": 100.0 * fb["frac_of_peak"], "rows_per_s": fb["rows_per_s"],
         "fwd": head["fwd"], "bwd": head["bwd"],
         "wall_s_timed_region_incl_flush": wall,
-        "copy_GBps": copy_gbps,
+        "copy_GBps_host_events": copy_gbps,
         "roofline": roofline,
         "per_workload": per,
     }

@@ -187,16 +187,22 @@ norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW,
 /* Static description of a status code (never NULL). */
 const char *norm_status_str(norm_status s);
 
-/* Timing hook for profilers and benchmarks.  Arms two caller-created
- * hipEvent_t handles for the NEXT entry-point call made by this host
- * thread: that call records `start` on its stream immediately before its
- * main streaming kernel and `stop` immediately after it, then disarms.
- * Either may be NULL to disarm.  Costs nothing when not armed.            */
-void norm_arm_kernel_events(void *start_event, void *stop_event);
+/* Timing hook for profilers and benchmarks.  `events` holds 2*n_pairs
+ * caller-created hipEvent_t handles.  The NEXT entry-point call made by this
+ * host thread launches its i-th kernel (i < n_pairs) with events[2i] and
+ * events[2i+1] attached to that kernel's own dispatch (hipExtLaunchKernel),
+ * so hipEventElapsedTime(events[2i], events[2i+1]) is the kernel's device
+ * time, and (events[0], events[2k-1]) spans a k-kernel call from the first
+ * kernel's start to the last kernel's end.  The call disarms the hook when
+ * it returns.  Costs nothing when not armed.  n_pairs <= 0 disarms.        */
+void norm_arm_kernel_events(void *const *events, int n_pairs);
 
-/* Name of the main streaming kernel the last call on this host thread
- * launched (for matching profiler traces); "" before any launch.         */
-const char *norm_last_kernel_name(void);
+/* Kernels launched by the last entry-point call on this host thread: their
+ * count, the name of the i-th (for matching profiler traces; "" when out of
+ * range), and the index of the main streaming kernel (-1 if none).       */
+int norm_last_kernel_count(void);
+const char *norm_last_kernel_name(int i);
+int norm_last_main_kernel(void);
 
 #ifdef __cplusplus
 }

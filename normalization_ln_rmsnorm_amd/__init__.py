@@ -4,10 +4,10 @@ The compute lives in libmi355norm.so (hand-written HIP kernels behind a C
 ABI, see include/mi355norm.h); ``normlib`` is the Python binding over it.
 """
 from .normlib import (ACT, NormError, bn_bwd, bn_fwd_eval, bn_fwd_train, bn_shape,
-                      bn_workspace_bytes, last_kernel_name, lib, ln_bwd,
+                      bn_workspace_bytes, last_kernels, lib, ln_bwd,
                       ln_bwd_workspace_bytes, ln_fwd, rms_bwd, rms_bwd_workspace_bytes,
                       rms_fwd, arm_kernel_events)
 
 __all__ = ["ACT", "NormError", "bn_bwd", "bn_fwd_eval", "bn_fwd_train", "bn_shape",
-           "bn_workspace_bytes", "last_kernel_name", "lib", "ln_bwd", "ln_bwd_workspace_bytes",
+           "bn_workspace_bytes", "last_kernels", "lib", "ln_bwd", "ln_bwd_workspace_bytes",
            "ln_fwd", "rms_bwd", "rms_bwd_workspace_bytes", "rms_fwd", "arm_kernel_events"]

@@ -9,12 +9,15 @@
 namespace mi355norm {
 
 namespace {
-struct ArmedEvents {
-    hipEvent_t start = nullptr;
-    hipEvent_t stop = nullptr;
+constexpr int kMaxKernelsPerCall = 16;
+struct CallState {
+    hipEvent_t events[2 * kMaxKernelsPerCall] = {};
+    int armed_pairs = 0;           // pairs armed for the current / next call
+    int count = 0;                 // kernels launched by the current / last call
+    int main_index = -1;
+    const char *names[kMaxKernelsPerCall] = {};
 };
-thread_local ArmedEvents g_armed;
-thread_local const char *g_last_kernel = "";
+thread_local CallState g_call;
 
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices] = {0};
@@ -33,15 +36,26 @@ int device_cu_count() {
     return n;
 }
 
-void hook_before(hipStream_t s, const char *kernel_name) {
-    g_last_kernel = kernel_name;
-    if (g_armed.start) (void)hipEventRecord(g_armed.start, s);
+void call_begin() {
+    g_call.count = 0;
+    g_call.main_index = -1;
 }
 
-void hook_after(hipStream_t s) {
-    if (g_armed.stop) (void)hipEventRecord(g_armed.stop, s);
-    g_armed.start = nullptr;
-    g_armed.stop = nullptr;
+void call_end() { g_call.armed_pairs = 0; }
+
+bool kernel_events(const char *name, bool is_main, hipEvent_t *start, hipEvent_t *stop) {
+    const int i = g_call.count;
+    if (i < kMaxKernelsPerCall) {
+        g_call.names[i] = name;
+        g_call.count = i + 1;
+    }
+    if (is_main) g_call.main_index = i;
+    if (i < g_call.armed_pairs && g_call.events[2 * i] && g_call.events[2 * i + 1]) {
+        *start = g_call.events[2 * i];
+        *stop = g_call.events[2 * i + 1];
+        return true;
+    }
+    return false;
 }
 
 }  // namespace mi355norm
@@ -60,9 +74,25 @@ extern "C" const char *norm_status_str(norm_status s) {
     return "unknown status";
 }
 
-extern "C" void norm_arm_kernel_events(void *start_event, void *stop_event) {
-    mi355norm::g_armed.start = static_cast<hipEvent_t>(start_event);
-    mi355norm::g_armed.stop = static_cast<hipEvent_t>(stop_event);
+extern "C" void norm_arm_kernel_events(void *const *events, int n_pairs) {
+    using namespace mi355norm;
+    if (!events || n_pairs <= 0) {
+        g_call.armed_pairs = 0;
+        return;
+    }
+    if (n_pairs > kMaxKernelsPerCall) n_pairs = kMaxKernelsPerCall;
+    for (int i = 0; i < 2 * n_pairs; ++i) g_call.events[i] = static_cast<hipEvent_t>(events[i]);
+    g_call.armed_pairs = n_pairs;
 }
 
-extern "C" const char *norm_last_kernel_name(void) { return mi355norm::g_last_kernel; }
+extern "C" int norm_last_kernel_count(void) {
+    return mi355norm::g_call.count < mi355norm::kMaxKernelsPerCall ? mi355norm::g_call.count
+                                                                   : mi355norm::kMaxKernelsPerCall;
+}
+
+extern "C" const char *norm_last_kernel_name(int i) {
+    if (i < 0 || i >= norm_last_kernel_count()) return "";
+    return mi355norm::g_call.names[i] ? mi355norm::g_call.names[i] : "";
+}
+
+extern "C" int norm_last_main_kernel(void) { return mi355norm::g_call.main_index; }

@@ -27,26 +27,29 @@
 //                       float64 triple per tile ([NormPage] "BatchNorm":
 //                       online correction by the difference from the previous
 //                       mean, no second pass; [MathPage] "Practice 2").
-//     bn_merge_kernel   one wave per channel merges the tile triples in
-//                       float64, saves mean and rstd, and applies the
-//                       momentum update to the running statistics.
-//     bn_apply_kernel   z = x * a_c + s_c (+ res), y = act(z), where
-//                       a_c = w_c * rstd_c and s_c = b_c - mean_c * a_c.
-//   forward (eval)      bn_apply_kernel with mean/rstd from running stats.
+//     bn_apply_kernel   each workgroup first merges its channel's tile
+//                       triples (float64, fixed order: every workgroup of a
+//                       channel gets the same bits), the channel's first
+//                       workgroup saves mean / rstd and applies the momentum
+//                       update, then z = x * a_c + s_c (+ res), y = act(z)
+//                       with a_c = w_c * rstd_c, s_c = b_c - mean_c * a_c.
+//   forward (eval)      bn_apply_kernel with mean / rstd from running stats.
 //   backward
 //     bn_bwd_reduce_kernel  recomputes z exactly as the forward did,
 //                       dz = dy * act'(z), stores dres = dz when a residual
 //                       was added, and sums dz, dz * (x - mean) and x - mean
 //                       per tile (float64 per element for float32 I/O,
 //                       float32 per thread for bf16; float64 beyond).
-//     bn_bwd_merge_kernel   one wave per channel: db = sum dz,
-//                       dw = rstd * sum dz (x - mean), and the three
-//                       coefficients of dx = k1*dz + k2*(x - mean) + k3.
-//     bn_bwd_dx_kernel  dz (re-read from dres, or recomputed from dy, x,
-//                       res), then dx.
+//     bn_bwd_dx_kernel  each workgroup adds its channel's tile sums, forms
+//                       db, dw and dx = k1*dz + k2*(x - mean) + k3 (the first
+//                       workgroup writes db, dw), then streams dz (re-read
+//                       from dres, or recomputed from dy, x, res) into dx.
+// Folding the per-channel merges into the following kernel saves a launch
+// and the gap between dependent kernels (several microseconds each).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <stdlib.h>
 
 #include <initializer_list>
 #include <type_traits>
@@ -59,7 +62,7 @@ namespace mi355norm {
 constexpr int kBnBlock = 256;
 constexpr int kBnWaves = kBnBlock / kWave;
 constexpr int kBnUnroll = 4;             // vectors in flight per thread per step
-constexpr int64_t kBnTileElems = 16384;  // target values per workgroup
+constexpr int64_t kBnTileBytes = 16384;  // target input bytes per workgroup
 
 // Per-channel scale and shift shared by the forward apply and the backward
 // recompute, so both evaluate z with identical float32 operations.
@@ -195,52 +198,67 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, double *__restrict__ part) {
     }
 }
 
-// ------------------------------------------------- forward: merge + EMA
-// One wave per channel; four channels per 256-thread block.
-__global__ void __launch_bounds__(kBnBlock)
-bn_merge_kernel(const double *__restrict__ part, int C, int tiles, float eps, float momentum,
-                float *__restrict__ running_mean, float *__restrict__ running_var,
-                float *__restrict__ save_mean, float *__restrict__ save_rstd) {
-    const int c = blockIdx.x * kBnWaves + threadIdx.x / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-    if (c >= C) return;  // whole wave exits together
-    WelfD acc{0.0, 0.0, 0.0};
-    for (int t = lane; t < tiles; t += kWave) {
-        const double *q = part + ((int64_t)c * tiles + t) * 3;
-        acc = welf_merge(acc, WelfD{q[0], q[1], q[2]});
-    }
+// ------------------------------------------- forward: channel statistics
+// Merges channel c's tile triples in float64 on the block's first wave
+// (lane-strided, then a butterfly of the symmetric merge) and shares the
+// result through LDS.  The order is fixed, so every workgroup of channel c
+// obtains the same bits.
+__device__ __forceinline__ WelfD merge_channel_tiles(const double *__restrict__ part, int c, int tiles) {
+    __shared__ WelfD sh;
+    if (threadIdx.x < kWave) {
+        WelfD acc{0.0, 0.0, 0.0};
+        for (int t = threadIdx.x; t < tiles; t += kWave) {
+            const double *q = part + ((int64_t)c * tiles + t) * 3;
+            acc = welf_merge(acc, WelfD{q[0], q[1], q[2]});
+        }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        WelfD o{shfl_xor_d(acc.n, m), shfl_xor_d(acc.mean, m), shfl_xor_d(acc.m2, m)};
-        acc = welf_merge(acc, o);
+        for (int m = 32; m >= 1; m >>= 1) {
+            WelfD o{shfl_xor_d(acc.n, m), shfl_xor_d(acc.mean, m), shfl_xor_d(acc.m2, m)};
+            acc = welf_merge(acc, o);
+        }
+        if (threadIdx.x == 0) sh = acc;
     }
-    if (lane == 0) {
-        const double n = acc.n;
-        const double var = acc.m2 / n;  // biased: the normalization variance
-        save_mean[c] = (float)acc.mean;
-        save_rstd[c] = (float)(1.0 / sqrt(var + (double)eps));
-        // [MathPage] "Practice 2": new = (1 - momentum) * old + momentum * batch;
-        // the running variance takes the unbiased batch variance.
-        const double m = (double)momentum;
-        if (running_mean) running_mean[c] = (float)((1.0 - m) * running_mean[c] + m * acc.mean);
-        if (running_var) running_var[c] = (float)((1.0 - m) * running_var[c] + m * (acc.m2 / (n - 1.0)));
-    }
+    __syncthreads();
+    return sh;
 }
 
 // ---------------------------------------------------- forward: apply
-// MODE 0: statistics from save_mean/save_rstd (training);
-// MODE 1: from running_mean/running_var with eps (eval).
+// MODE 0 (training): mean and rstd come from the merged tile statistics
+// (biased variance); the channel's first workgroup also writes them to
+// save_mean / save_rstd and applies the momentum update ([MathPage]
+// "Practice 2": new = (1 - momentum) * old + momentum * batch, the running
+// variance taking the unbiased batch variance).
+// MODE 1 (eval): mean = running_mean, rstd = 1 / sqrt(running_var + eps).
+// Then z = x * a_c + s_c (+ res), y = act(z).
 template <typename T, int V, int ACT, bool RES, int MODE>
 __global__ void __launch_bounds__(kBnBlock)
 bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__restrict__ w,
-                const T *__restrict__ b, const float *__restrict__ stat_mean,
-                const float *__restrict__ stat_scale, float eps, T *__restrict__ y, BnGeom g) {
+                const T *__restrict__ b, const double *__restrict__ part, float eps, float momentum,
+                float *__restrict__ running_mean, float *__restrict__ running_var,
+                float *__restrict__ save_mean, float *__restrict__ save_rstd, T *__restrict__ y,
+                BnGeom g) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
+    constexpr bool kFast = sizeof(T) == 2;
     int c; int64_t n0, n1;
     tile_of_block(g, &c, &n0, &n1);
-    const float mean = stat_mean[c];
-    const float rstd = MODE == 0 ? stat_scale[c] : 1.0f / sqrtf(stat_scale[c] + eps);
+    float mean, rstd;
+    if (MODE == 0) {
+        const WelfD st = merge_channel_tiles(part, c, g.tiles);
+        mean = (float)st.mean;
+        rstd = (float)(1.0 / sqrt(st.m2 / st.n + (double)eps));
+        if (n0 == 0 && threadIdx.x == 0) {
+            save_mean[c] = mean;
+            save_rstd[c] = rstd;
+            const double m = (double)momentum;
+            if (running_mean) running_mean[c] = (float)((1.0 - m) * running_mean[c] + m * st.mean);
+            if (running_var)
+                running_var[c] = (float)((1.0 - m) * running_var[c] + m * (st.m2 / (st.n - 1.0)));
+        }
+    } else {
+        mean = running_mean[c];
+        rstd = 1.0f / sqrtf(running_var[c] + eps);
+    }
     float a, s;
     bn_coeffs(mean, rstd, w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a, &s);
     const int64_t nvp = g.HW / V;
@@ -268,7 +286,7 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
                     for (int e = 0; e < V; ++e) {
                         float z = fmaf(f[e], a, s);
                         if (RES) z += rf[e];
-                        o[e] = act_fwd<ACT>(z);
+                        o[e] = act_fwd<ACT, kFast>(z);
                     }
                     vstore_stream<T, V>(y + off + v * V, VT::pack(o));
                 }
@@ -328,7 +346,7 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
                         if (ACT != kActNone) {
                             float z = fmaf(xf[e], a, s);
                             if (RES) z += rf[e];
-                            dz[e] = df[e] * act_grad<ACT>(z);
+                            dz[e] = df[e] * act_grad<ACT, sizeof(T) == 2>(z);
                         } else {
                             dz[e] = df[e];
                         }
@@ -368,48 +386,43 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
     }
 }
 
-// ----------------------------------------------------- backward: merge
-// With m the saved (float32) mean, the tile sums are S_dz = sum dz,
-// S_dzx = sum dz (x - m) and S_xc = sum (x - m).  The exact batch mean is
+// ------------------------------------------- backward: channel sums
+// Adds channel c's three tile sums in float64 on the block's first wave
+// (fixed order, identical in every workgroup of the channel).
+__device__ __forceinline__ void sum_channel_tiles(const double *__restrict__ part, int c, int tiles,
+                                                  double out[3]) {
+    __shared__ double sh[3];
+    if (threadIdx.x < kWave) {
+        double s0 = 0.0, s1 = 0.0, s2 = 0.0;
+        for (int t = threadIdx.x; t < tiles; t += kWave) {
+            const double *q = part + ((int64_t)c * tiles + t) * 3;
+            s0 += q[0];
+            s1 += q[1];
+            s2 += q[2];
+        }
+        s0 = wave_sum_d(s0);
+        s1 = wave_sum_d(s1);
+        s2 = wave_sum_d(s2);
+        if (threadIdx.x == 0) {
+            sh[0] = s0;
+            sh[1] = s1;
+            sh[2] = s2;
+        }
+    }
+    __syncthreads();
+    out[0] = sh[0];
+    out[1] = sh[1];
+    out[2] = sh[2];
+}
+
+// ----------------------------------------------------- backward: pass 2
+// With m the saved (float32) mean, the channel sums are S_dz = sum dz,
+// S_dzx = sum dz (x - m) and S_xc = sum (x - m); the exact batch mean is
 // m + S_xc / n, so
 //   db = S_dz,   dw = rstd * (S_dzx - S_xc * S_dz / n)   (= sum dz * xhat)
 // and dx = (w rstd / n)(n dz - db - xhat dw) = k1 dz + k2 (x - m) + k3 with
 //   k1 = w rstd,  k2 = -w rstd^2 dw / n,  k3 = -w rstd db / n - k2 S_xc / n.
-template <typename T>
-__global__ void __launch_bounds__(kBnBlock)
-bn_bwd_merge_kernel(const double *__restrict__ part, int C, int tiles, double n_total,
-                    const T *__restrict__ w, const float *__restrict__ save_rstd,
-                    T *__restrict__ dw, T *__restrict__ db, float *__restrict__ coef) {
-    const int c = blockIdx.x * kBnWaves + threadIdx.x / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-    if (c >= C) return;
-    double s0 = 0.0, s1 = 0.0, s2 = 0.0;
-    for (int t = lane; t < tiles; t += kWave) {
-        const double *q = part + ((int64_t)c * tiles + t) * 3;
-        s0 += q[0];
-        s1 += q[1];
-        s2 += q[2];
-    }
-    s0 = wave_sum_d(s0);
-    s1 = wave_sum_d(s1);
-    s2 = wave_sum_d(s2);
-    if (lane == 0) {
-        const double r = (double)save_rstd[c];
-        const double wc = w ? (double)ld1(w + c) : 1.0;
-        const double mean_shift = s2 / n_total;  // exact mean minus saved mean
-        const double dbeta = s0;
-        const double dgamma = r * (s1 - mean_shift * s0);
-        if (db) st1(db + c, (float)dbeta);
-        if (dw) st1(dw + c, (float)dgamma);
-        const double k2 = -wc * r * r * dgamma / n_total;
-        coef[c * 4 + 0] = (float)(wc * r);
-        coef[c * 4 + 1] = (float)k2;
-        coef[c * 4 + 2] = (float)(-wc * r * dbeta / n_total - k2 * mean_shift);
-        coef[c * 4 + 3] = 0.0f;
-    }
-}
-
-// ----------------------------------------------------- backward: pass 2
+// The channel's first workgroup writes dw and db.
 // DZ_SRC 0: dz = dy (no activation, no residual recompute needed);
 //        1: dz re-read from dres (written by pass 1, exact in float32);
 //        2: dz recomputed from dy, x (and res) as in pass 1.
@@ -418,15 +431,31 @@ __global__ void __launch_bounds__(kBnBlock)
 bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__restrict__ res,
                  const T *__restrict__ dres, const T *__restrict__ w, const T *__restrict__ b,
                  const float *__restrict__ save_mean, const float *__restrict__ save_rstd,
-                 const float *__restrict__ coef, T *__restrict__ dx, BnGeom g) {
+                 const double *__restrict__ part, double n_total, T *__restrict__ dw, T *__restrict__ db,
+                 T *__restrict__ dx, BnGeom g) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
+    constexpr bool kFast = sizeof(T) == 2;
     int c; int64_t n0, n1;
     tile_of_block(g, &c, &n0, &n1);
+    double sums[3];
+    sum_channel_tiles(part, c, g.tiles, sums);
     const float mean = save_mean[c];
+    const float rstd_f = save_rstd[c];
+    const float wc_f = w ? ld1(w + c) : 1.0f;
+    const double r = (double)rstd_f, wc = (double)wc_f;
+    const double mean_shift = sums[2] / n_total;  // exact mean minus saved mean
+    const double dbeta = sums[0];
+    const double dgamma = r * (sums[1] - mean_shift * sums[0]);
+    if (n0 == 0 && threadIdx.x == 0) {
+        if (db) st1(db + c, (float)dbeta);
+        if (dw) st1(dw + c, (float)dgamma);
+    }
+    const double k2d = -wc * r * r * dgamma / n_total;
+    const float k1 = (float)(wc * r), k2 = (float)k2d;
+    const float k3 = (float)(-wc * r * dbeta / n_total - k2d * mean_shift);
     float a = 0.0f, s = 0.0f;
-    if (DZ_SRC == 2) bn_coeffs(mean, save_rstd[c], w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a, &s);
-    const float k1 = coef[c * 4 + 0], k2 = coef[c * 4 + 1], k3 = coef[c * 4 + 2];
+    if (DZ_SRC == 2) bn_coeffs(mean, rstd_f, wc_f, b ? ld1(b + c) : 0.0f, &a, &s);
     const int64_t nvp = g.HW / V;
     const T *dzsrc = DZ_SRC == 1 ? dres : dy;
 
@@ -457,7 +486,7 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
                         if (DZ_SRC == 2 && ACT != kActNone) {
                             float z = fmaf(xf[e], a, s);
                             if (RES) z += rf[e];
-                            dz = df[e] * act_grad<ACT>(z);
+                            dz = df[e] * act_grad<ACT, kFast>(z);
                         }
                         o[e] = fmaf(k1, dz, fmaf(k2, xf[e] - mean, k3));
                     }
@@ -469,12 +498,25 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
 }
 
 // ------------------------------------------------------------- host side
-static BnGeom make_geom(int64_t Nb, int64_t C, int64_t HW) {
+// Values per workgroup: 16 KiB of input (4096 float32 or 8192 bf16 values,
+// rounded up to whole planes), the best of a sweep over the two BatchNorm
+// workloads.  MI355NORM_BN_TILE (values) overrides it for tuning sweeps; it
+// is read per call, so the workspace query and the call must see the same.
+static int64_t tile_elems(norm_dtype dt) {
+    const char *e = getenv("MI355NORM_BN_TILE");
+    if (e && *e) {
+        const long long v = atoll(e);
+        if (v >= 256 && v <= (1LL << 26)) return v;
+    }
+    return kBnTileBytes / (int64_t)dtype_size(dt);
+}
+
+static BnGeom make_geom(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW) {
     BnGeom g;
     g.Nb = Nb;
     g.HW = HW;
     g.C = (int)C;
-    int64_t ppb = HW > 0 ? ceil_div(kBnTileElems, HW) : 1;
+    int64_t ppb = HW > 0 ? ceil_div(tile_elems(dt), HW) : 1;
     if (ppb > Nb) ppb = Nb > 0 ? Nb : 1;
     if (ppb < 1) ppb = 1;
     g.ppb = (int)ppb;
@@ -497,14 +539,11 @@ static bool bn_vec_ok(norm_dtype dt, int64_t HW, std::initializer_list<const voi
     return true;
 }
 
-static size_t ws_layout(int64_t Nb, int64_t C, int64_t HW, size_t *coef_off) {
-    const BnGeom g = make_geom(Nb, C, HW);
-    const size_t fwd = (size_t)C * g.tiles * 3 * sizeof(double);
-    const size_t bwd_part = (size_t)C * g.tiles * 3 * sizeof(double);
-    const size_t coef_at = (bwd_part + 255) & ~(size_t)255;
-    const size_t bwd = coef_at + (size_t)C * 4 * sizeof(float);
-    if (coef_off) *coef_off = coef_at;
-    return fwd > bwd ? fwd : bwd;
+// Workspace: one float64 triple per (channel, tile) -- the forward's
+// (count, mean, M2) or the backward's three sums.
+static size_t ws_layout(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW) {
+    const BnGeom g = make_geom(dt, Nb, C, HW);
+    return (size_t)C * g.tiles * 3 * sizeof(double);
 }
 
 template <typename T, int V>
@@ -513,10 +552,9 @@ static norm_status launch_fwd_train(const BnGeom &g, hipStream_t st, norm_act ac
                                     float *rm, float *rv, float *sm, float *sr, void *y, void *ws) {
     const dim3 grid((unsigned)(g.C * (int64_t)g.tiles));
     double *part = static_cast<double *>(ws);
-    hipLaunchKernelGGL((bn_stats_kernel<T, V>), grid, dim3(kBnBlock), 0, st, (const T *)x, g, part);
-    hipLaunchKernelGGL(bn_merge_kernel, dim3((unsigned)ceil_div(g.C, kBnWaves)), dim3(kBnBlock), 0, st,
-                       (const double *)part, g.C, g.tiles, eps, momentum, rm, rv, sm, sr);
-    using fn_t = void (*)(const T *, const T *, const T *, const T *, const float *, const float *, float, T *, BnGeom);
+    launch("bn_stats_kernel", false, bn_stats_kernel<T, V>, grid, dim3(kBnBlock), 0, st, (const T *)x, g, part);
+    using fn_t = void (*)(const T *, const T *, const T *, const T *, const double *, float, float, float *,
+                          float *, float *, float *, T *, BnGeom);
     fn_t fn = nullptr;
     const bool r = res != nullptr;
     switch (act) {
@@ -524,10 +562,8 @@ static norm_status launch_fwd_train(const BnGeom &g, hipStream_t st, norm_act ac
     case NORM_ACT_RELU: fn = r ? bn_apply_kernel<T, V, kActRelu, true, 0> : bn_apply_kernel<T, V, kActRelu, false, 0>; break;
     case NORM_ACT_GELU: fn = r ? bn_apply_kernel<T, V, kActGelu, true, 0> : bn_apply_kernel<T, V, kActGelu, false, 0>; break;
     }
-    hook_before(st, "bn_apply_kernel<train>");
-    hipLaunchKernelGGL(fn, grid, dim3(kBnBlock), 0, st, (const T *)x, (const T *)res, (const T *)w, (const T *)b,
-                       (const float *)sm, (const float *)sr, eps, (T *)y, g);
-    hook_after(st);
+    launch("bn_apply_kernel<train>", true, fn, grid, dim3(kBnBlock), 0, st, (const T *)x, (const T *)res,
+           (const T *)w, (const T *)b, (const double *)part, eps, momentum, rm, rv, sm, sr, (T *)y, g);
     return launch_status();
 }
 
@@ -536,7 +572,8 @@ static norm_status launch_fwd_eval(const BnGeom &g, hipStream_t st, norm_act act
                                    const void *res, const void *w, const void *b, const float *rm,
                                    const float *rv, void *y) {
     const dim3 grid((unsigned)(g.C * (int64_t)g.tiles));
-    using fn_t = void (*)(const T *, const T *, const T *, const T *, const float *, const float *, float, T *, BnGeom);
+    using fn_t = void (*)(const T *, const T *, const T *, const T *, const double *, float, float, float *,
+                          float *, float *, float *, T *, BnGeom);
     fn_t fn = nullptr;
     const bool r = res != nullptr;
     switch (act) {
@@ -544,62 +581,62 @@ static norm_status launch_fwd_eval(const BnGeom &g, hipStream_t st, norm_act act
     case NORM_ACT_RELU: fn = r ? bn_apply_kernel<T, V, kActRelu, true, 1> : bn_apply_kernel<T, V, kActRelu, false, 1>; break;
     case NORM_ACT_GELU: fn = r ? bn_apply_kernel<T, V, kActGelu, true, 1> : bn_apply_kernel<T, V, kActGelu, false, 1>; break;
     }
-    hook_before(st, "bn_apply_kernel<eval>");
-    hipLaunchKernelGGL(fn, grid, dim3(kBnBlock), 0, st, (const T *)x, (const T *)res, (const T *)w, (const T *)b,
-                       rm, rv, eps, (T *)y, g);
-    hook_after(st);
+    // Eval reads the running statistics; they are not written.
+    launch("bn_apply_kernel<eval>", true, fn, grid, dim3(kBnBlock), 0, st, (const T *)x, (const T *)res,
+           (const T *)w, (const T *)b, (const double *)nullptr, eps, 0.0f, const_cast<float *>(rm),
+           const_cast<float *>(rv), (float *)nullptr, (float *)nullptr, (T *)y, g);
     return launch_status();
 }
 
 template <typename T, int V, int ACT>
 static void launch_bwd_act(const BnGeom &g, hipStream_t st, bool has_res, const void *dy, const void *x,
                            const void *res, const void *w, const void *b, const float *sm, const float *sr,
-                           void *dx, void *dres, void *dw, void *db, void *ws, size_t coef_off) {
+                           void *dx, void *dres, void *dw, void *db, void *ws) {
     const dim3 grid((unsigned)(g.C * (int64_t)g.tiles));
+    const dim3 blk(kBnBlock);
     double *part = static_cast<double *>(ws);
-    float *coef = reinterpret_cast<float *>(static_cast<char *>(ws) + coef_off);
+    const double n_total = (double)g.Nb * (double)g.HW;
+    // The main (largest) kernel: pass 1 with a residual (it reads dy, x, res
+    // and writes dres), pass 2 otherwise.
     if (has_res)
-        hipLaunchKernelGGL((bn_bwd_reduce_kernel<T, V, ACT, true>), grid, dim3(kBnBlock), 0, st, (const T *)dy,
-                           (const T *)x, (const T *)res, (const T *)w, (const T *)b, sm, sr, (T *)dres, g, part);
+        launch("bn_bwd_reduce_kernel", true, bn_bwd_reduce_kernel<T, V, ACT, true>, grid, blk, 0, st,
+               (const T *)dy, (const T *)x, (const T *)res, (const T *)w, (const T *)b, sm, sr, (T *)dres, g, part);
     else
-        hipLaunchKernelGGL((bn_bwd_reduce_kernel<T, V, ACT, false>), grid, dim3(kBnBlock), 0, st, (const T *)dy,
-                           (const T *)x, (const T *)res, (const T *)w, (const T *)b, sm, sr, (T *)dres, g, part);
-    hipLaunchKernelGGL(bn_bwd_merge_kernel<T>, dim3((unsigned)ceil_div(g.C, kBnWaves)), dim3(kBnBlock), 0, st,
-                       (const double *)part, g.C, g.tiles, (double)g.Nb * (double)g.HW, (const T *)w, sr, (T *)dw,
-                       (T *)db, coef);
+        launch("bn_bwd_reduce_kernel", false, bn_bwd_reduce_kernel<T, V, ACT, false>, grid, blk, 0, st,
+               (const T *)dy, (const T *)x, (const T *)res, (const T *)w, (const T *)b, sm, sr, (T *)dres, g, part);
     // dz for pass 2: float32 dres holds dz exactly; bf16 dres is rounded, so
     // there dz is recomputed from dy and x (and res).
     const bool fp32 = sizeof(T) == 4;
-    hook_before(st, "bn_bwd_dx_kernel");
+    const bool main = !has_res;
+    const double *cp = part;
     if (ACT == kActNone && !has_res) {
-        hipLaunchKernelGGL((bn_bwd_dx_kernel<T, V, ACT, false, 0>), grid, dim3(kBnBlock), 0, st, (const T *)dy,
-                           (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr,
-                           (const float *)coef, (T *)dx, g);
+        launch("bn_bwd_dx_kernel", main, bn_bwd_dx_kernel<T, V, ACT, false, 0>, grid, blk, 0, st, (const T *)dy,
+               (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr, cp, n_total,
+               (T *)dw, (T *)db, (T *)dx, g);
     } else if (has_res && (fp32 || ACT == kActNone)) {
-        hipLaunchKernelGGL((bn_bwd_dx_kernel<T, V, ACT, true, 1>), grid, dim3(kBnBlock), 0, st, (const T *)dy,
-                           (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr,
-                           (const float *)coef, (T *)dx, g);
+        launch("bn_bwd_dx_kernel", main, bn_bwd_dx_kernel<T, V, ACT, true, 1>, grid, blk, 0, st, (const T *)dy,
+               (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr, cp, n_total,
+               (T *)dw, (T *)db, (T *)dx, g);
     } else if (has_res) {
-        hipLaunchKernelGGL((bn_bwd_dx_kernel<T, V, ACT, true, 2>), grid, dim3(kBnBlock), 0, st, (const T *)dy,
-                           (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr,
-                           (const float *)coef, (T *)dx, g);
+        launch("bn_bwd_dx_kernel", main, bn_bwd_dx_kernel<T, V, ACT, true, 2>, grid, blk, 0, st, (const T *)dy,
+               (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr, cp, n_total,
+               (T *)dw, (T *)db, (T *)dx, g);
     } else {
-        hipLaunchKernelGGL((bn_bwd_dx_kernel<T, V, ACT, false, 2>), grid, dim3(kBnBlock), 0, st, (const T *)dy,
-                           (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr,
-                           (const float *)coef, (T *)dx, g);
+        launch("bn_bwd_dx_kernel", main, bn_bwd_dx_kernel<T, V, ACT, false, 2>, grid, blk, 0, st, (const T *)dy,
+               (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr, cp, n_total,
+               (T *)dw, (T *)db, (T *)dx, g);
     }
-    hook_after(st);
 }
 
 template <typename T, int V>
 static norm_status launch_bwd(const BnGeom &g, hipStream_t st, norm_act act, const void *dy, const void *x,
                               const void *res, const void *w, const void *b, const float *sm, const float *sr,
-                              void *dx, void *dres, void *dw, void *db, void *ws, size_t coef_off) {
+                              void *dx, void *dres, void *dw, void *db, void *ws) {
     const bool r = res != nullptr;
     switch (act) {
-    case NORM_ACT_NONE: launch_bwd_act<T, V, kActNone>(g, st, r, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws, coef_off); break;
-    case NORM_ACT_RELU: launch_bwd_act<T, V, kActRelu>(g, st, r, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws, coef_off); break;
-    case NORM_ACT_GELU: launch_bwd_act<T, V, kActGelu>(g, st, r, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws, coef_off); break;
+    case NORM_ACT_NONE: launch_bwd_act<T, V, kActNone>(g, st, r, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws); break;
+    case NORM_ACT_RELU: launch_bwd_act<T, V, kActRelu>(g, st, r, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws); break;
+    case NORM_ACT_GELU: launch_bwd_act<T, V, kActGelu>(g, st, r, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws); break;
     }
     return launch_status();
 }
@@ -612,13 +649,14 @@ using namespace mi355norm;
 
 extern "C" size_t bn_workspace_bytes(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW) {
     if (check_bn(dt, Nb, C, HW) != NORM_OK) return 0;
-    return ws_layout(Nb, C, HW, nullptr);
+    return ws_layout(dt, Nb, C, HW);
 }
 
 extern "C" norm_status bn_fwd_train(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, float eps, float momentum,
                                     norm_act act, const void *x, const void *res, const void *w, const void *b,
                                     float *running_mean, float *running_var, float *save_mean, float *save_rstd,
                                     void *y, void *ws, size_t ws_bytes, void *stream) {
+    CallScope scope;
     norm_status s = check_bn(dt, Nb, C, HW);
     if (s != NORM_OK) return s;
     if (!act_ok(act)) return NORM_ERR_ACT;
@@ -626,8 +664,8 @@ extern "C" norm_status bn_fwd_train(norm_dtype dt, int64_t Nb, int64_t C, int64_
     if (C == 0) return NORM_OK;
     if (Nb * HW < 2) return NORM_ERR_ARG;  // the unbiased running variance needs n >= 2
     if (!x || !y || !save_mean || !save_rstd) return NORM_ERR_NULL;
-    if (!ws || ws_bytes < ws_layout(Nb, C, HW, nullptr)) return NORM_ERR_WORKSPACE;
-    const BnGeom g = make_geom(Nb, C, HW);
+    if (!ws || ws_bytes < ws_layout(dt, Nb, C, HW)) return NORM_ERR_WORKSPACE;
+    const BnGeom g = make_geom(dt, Nb, C, HW);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool vec = bn_vec_ok(dt, HW, {x, res, y});
     if (dt == NORM_F32)
@@ -640,13 +678,14 @@ extern "C" norm_status bn_fwd_train(norm_dtype dt, int64_t Nb, int64_t C, int64_
 extern "C" norm_status bn_fwd_eval(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, float eps, norm_act act,
                                    const void *x, const void *res, const void *w, const void *b,
                                    const float *running_mean, const float *running_var, void *y, void *stream) {
+    CallScope scope;
     norm_status s = check_bn(dt, Nb, C, HW);
     if (s != NORM_OK) return s;
     if (!act_ok(act)) return NORM_ERR_ACT;
     if (!(eps >= 0.0f)) return NORM_ERR_ARG;
     if (C == 0 || Nb * HW == 0) return NORM_OK;
     if (!x || !y || !running_mean || !running_var) return NORM_ERR_NULL;
-    const BnGeom g = make_geom(Nb, C, HW);
+    const BnGeom g = make_geom(dt, Nb, C, HW);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool vec = bn_vec_ok(dt, HW, {x, res, y});
     if (dt == NORM_F32)
@@ -660,6 +699,7 @@ extern "C" norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, 
                               const void *x, const void *res, const void *w, const void *b, const float *save_mean,
                               const float *save_rstd, void *dx, void *dres, void *dw, void *db, void *ws,
                               size_t ws_bytes, void *stream) {
+    CallScope scope;
     norm_status s = check_bn(dt, Nb, C, HW);
     if (s != NORM_OK) return s;
     if (!act_ok(act)) return NORM_ERR_ACT;
@@ -667,14 +707,13 @@ extern "C" norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, 
     if (Nb * HW < 2) return NORM_ERR_ARG;
     if (!dy || !x || !dx || !save_mean || !save_rstd) return NORM_ERR_NULL;
     if (res && !dres) return NORM_ERR_NULL;
-    size_t coef_off = 0;
-    if (!ws || ws_bytes < ws_layout(Nb, C, HW, &coef_off)) return NORM_ERR_WORKSPACE;
-    const BnGeom g = make_geom(Nb, C, HW);
+    if (!ws || ws_bytes < ws_layout(dt, Nb, C, HW)) return NORM_ERR_WORKSPACE;
+    const BnGeom g = make_geom(dt, Nb, C, HW);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool vec = bn_vec_ok(dt, HW, {dy, x, res, dx, dres});
     if (dt == NORM_F32)
-        return vec ? launch_bwd<float, 4>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws, coef_off)
-                   : launch_bwd<float, 1>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws, coef_off);
-    return vec ? launch_bwd<bf16_t, 8>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws, coef_off)
-               : launch_bwd<bf16_t, 1>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws, coef_off);
+        return vec ? launch_bwd<float, 4>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws)
+                   : launch_bwd<float, 1>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws);
+    return vec ? launch_bwd<bf16_t, 8>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws)
+               : launch_bwd<bf16_t, 1>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws);
 }

@@ -1,6 +1,9 @@
 // norm_device.hpp -- device-side building blocks for the gfx950 kernels:
 // element I/O (float32 / bf16, 128-bit vectors), wave64 reductions (DPP,
 // ds_swizzle, readlane), and the activation functions.
+//
+// [ActPage] = "Operator fusion in practice: attorch's activation and dropout
+// fusion kernels".
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -162,23 +165,61 @@ __device__ __forceinline__ double shfl_xor_d(double v, int mask) {
 // ReLU and the exact error-function GELU ([ActPage] sections 5-6), computed
 // in float32.  GELU(z) = z * Phi(z), Phi(z) = (1 + erf(z / sqrt 2)) / 2;
 // GELU'(z) = Phi(z) + z * phi(z), phi(z) = exp(-z^2 / 2) / sqrt(2 pi).
+//
+// Two evaluations of Phi:
+//  * accurate (FAST = false): the device erff and expf, for float32 I/O,
+//    whose 1e-5 tolerance on channel sums over millions of values leaves no
+//    room for a systematic per-element error;
+//  * fast (FAST = true), for bf16 I/O, where the BatchNorm GELU backward is
+//    otherwise bound by VALU time: Abramowitz & Stegun, Handbook of
+//    Mathematical Functions, eq. 7.1.26 (Hastings' approximation),
+//    erfc(u) ~= t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-u^2),
+//    t = 1 / (1 + p u), u >= 0, with |error in erf| <= 1.5e-7.  With
+//    u = |z| / sqrt 2 the exp(-u^2) is exp(-z^2 / 2), the same factor phi
+//    needs, so Phi and phi share one exp; in float32 the result is within
+//    3e-7 of Phi (and of GELU') everywhere -- far inside 2 bf16 ulp.
+//    The coefficients below are A&S's a1..a5 halved (they give Phi(-|z|)
+//    = erfc(u) / 2 directly).
 enum Act : int { kActNone = 0, kActRelu = 1, kActGelu = 2 };
 
 constexpr float kInvSqrt2 = 0.70710678118654752440f;
 constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
+constexpr float kNegHalfLog2e = -0.72134752044448170368f;  // -log2(e) / 2
 
-template <int ACT> __device__ __forceinline__ float act_fwd(float z) {
-    if constexpr (ACT == kActRelu) return z > 0.0f ? z : 0.0f;
-    else if constexpr (ACT == kActGelu) return 0.5f * z * (1.0f + erff(z * kInvSqrt2));
-    else return z;
+struct NormalPdfCdf {
+    float e;    // exp(-z^2 / 2)
+    float Phi;  // standard normal CDF at z
+};
+
+template <bool FAST> __device__ __forceinline__ NormalPdfCdf normal_pdf_cdf(float z) {
+    if constexpr (FAST) {
+        const float e = __builtin_amdgcn_exp2f(z * z * kNegHalfLog2e);
+        const float u = fabsf(z) * kInvSqrt2;
+        const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, u, 1.0f));
+        float p = fmaf(t, 0.5307027145f, -0.7265760135f);
+        p = fmaf(t, p, 0.7107068705f);
+        p = fmaf(t, p, -0.142248368f);
+        p = fmaf(t, p, 0.127414796f);
+        const float q = p * t * e;  // Phi(-|z|)
+        return NormalPdfCdf{e, z >= 0.0f ? 1.0f - q : q};
+    } else {
+        return NormalPdfCdf{expf(-0.5f * z * z), 0.5f * (1.0f + erff(z * kInvSqrt2))};
+    }
 }
 
-template <int ACT> __device__ __forceinline__ float act_grad(float z) {
+template <int ACT, bool FAST = false> __device__ __forceinline__ float act_fwd(float z) {
+    if constexpr (ACT == kActRelu) return z > 0.0f ? z : 0.0f;
+    else if constexpr (ACT == kActGelu) {
+        if constexpr (FAST) return z * normal_pdf_cdf<true>(z).Phi;
+        else return 0.5f * z * (1.0f + erff(z * kInvSqrt2));
+    } else return z;
+}
+
+template <int ACT, bool FAST = false> __device__ __forceinline__ float act_grad(float z) {
     if constexpr (ACT == kActRelu) return z > 0.0f ? 1.0f : 0.0f;
     else if constexpr (ACT == kActGelu) {
-        float Phi = 0.5f * (1.0f + erff(z * kInvSqrt2));
-        float phi = expf(-0.5f * z * z) * kInvSqrt2Pi;
-        return fmaf(z, phi, Phi);
+        const NormalPdfCdf n = normal_pdf_cdf<FAST>(z);
+        return fmaf(z * kInvSqrt2Pi, n.e, n.Phi);
     } else return 1.0f;
 }
 

@@ -3,6 +3,7 @@
 // error mapping.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -18,9 +19,27 @@ inline bool dtype_ok(norm_dtype dt) { return dt == NORM_F32 || dt == NORM_BF16; 
 // Compute units of the current device (cached per device id).
 int device_cu_count();
 
-// Timing hook (see norm_arm_kernel_events): called around the main kernel.
-void hook_before(hipStream_t s, const char *kernel_name);
-void hook_after(hipStream_t s);
+// Per-call kernel bookkeeping behind norm_arm_kernel_events: every entry
+// point opens a CallScope; every kernel goes through launch(), which
+// attaches the armed event pair (if any) to that kernel's dispatch.
+void call_begin();
+void call_end();
+bool kernel_events(const char *name, bool is_main, hipEvent_t *start, hipEvent_t *stop);
+
+struct CallScope {
+    CallScope() { call_begin(); }
+    ~CallScope() { call_end(); }
+};
+
+template <typename F, typename... Args>
+inline void launch(const char *name, bool is_main, F fn, dim3 grid, dim3 block, size_t shmem,
+                   hipStream_t s, Args... args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (kernel_events(name, is_main, &e0, &e1))
+        hipExtLaunchKernelGGL(fn, grid, block, (uint32_t)shmem, s, e0, e1, 0u, args...);
+    else
+        hipLaunchKernelGGL(fn, grid, block, shmem, s, args...);
+}
 
 // Map the launch status of the kernels just enqueued.
 inline norm_status launch_status() {

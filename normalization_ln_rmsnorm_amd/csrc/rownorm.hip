@@ -39,6 +39,7 @@ namespace mi355norm {
 constexpr int kMaxWavesPerBlock = 16;
 constexpr int kMaxBwdBlocksPerCU = 8;  // cap on persistent backward blocks per CU
 
+
 template <typename VT> __device__ __forceinline__ typename VT::raw_t ones_raw() {
     float f[VT::n];
 #pragma unroll
@@ -90,6 +91,12 @@ __device__ __forceinline__ void row_sum2(float &a, float &b, int tpr, float (*ld
     }
 }
 
+// The row is kept in registers in its packed I/O form and unpacked again
+// for each pass over it; `opaque` stops the compiler from keeping the first
+// unpacked copy alive instead (float32 copies of a bf16 row double the
+// register footprint and halve the number of waves a CU can hold).
+template <typename R> __device__ __forceinline__ void opaque(R &r) { asm volatile("" : "+v"(r)); }
+
 // ------------------------------------------------------------------ forward
 // LayerNorm ([NormPage] "LayerNorm" section): mean, then the sum of squared
 // deviations (exact two-pass over the register-resident row), rstd by rsqrt,
@@ -121,40 +128,66 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
         }
     }
 
-    for (int64_t base = (int64_t)blockIdx.x * rpb; base < M; base += (int64_t)gridDim.x * rpb) {
+    // Software pipelined: the next row's loads are issued before this row is
+    // reduced and stored, so every wave keeps loads in flight.
+    const int64_t step = (int64_t)gridDim.x * rpb;
+    int64_t base = (int64_t)blockIdx.x * rpb;
+    raw_t xr[IT];
+    {
         const int64_t row = base + slot_in_block;
-        const bool active = row < M;
-        const T *xrow = x + row * N;
-
-        float xf[IT][V];
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const int v = lane + k * tpr;
-            raw_t r = zeros_raw<VT>();
-            if (active && v < nv) r = vload_stream<T, V>(xrow + (int64_t)v * V);
-            VT::unpack(r, xf[k]);
+            xr[k] = zeros_raw<VT>();
+            if (row < M && v < nv) xr[k] = vload_stream<T, V>(x + row * N + (int64_t)v * V);
+        }
+    }
+    for (; base < M; base += step) {
+        const int64_t row = base + slot_in_block;
+        const bool active = row < M;
+        const int64_t nrow = row + step;
+        raw_t nx[IT];
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int v = lane + k * tpr;
+            nx[k] = zeros_raw<VT>();
+            if (nrow < M && v < nv) nx[k] = vload_stream<T, V>(x + nrow * N + (int64_t)v * V);
+        }
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {  // keep w, b packed (no hoisted float copies)
+            opaque(wr[k]);
+            if (!RMS) opaque(br[k]);
         }
 
         float mean = 0.0f;
         if (!RMS) {
             float s = 0.0f;
 #pragma unroll
-            for (int k = 0; k < IT; ++k)
+            for (int k = 0; k < IT; ++k) {
+                float f[V];
+                VT::unpack(xr[k], f);
 #pragma unroll
-                for (int e = 0; e < V; ++e) s += xf[k][e];
+                for (int e = 0; e < V; ++e) s += f[e];
+            }
             mean = row_sum(s, tpr, lds, 0) * inv_n;
+#pragma unroll
+            for (int k = 0; k < IT; ++k) opaque(xr[k]);
         }
         float q = 0.0f;
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const bool valid = lane + k * tpr < nv;
+            float f[V];
+            VT::unpack(xr[k], f);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                const float d = xf[k][e] - mean;
+                const float d = f[e] - mean;
                 q += valid ? d * d : 0.0f;
             }
         }
         const float rstd = rsqrtf(row_sum(q, tpr, lds, 1) * inv_n + eps);
+#pragma unroll
+        for (int k = 0; k < IT; ++k) opaque(xr[k]);
 
         if (active) {
             T *yrow = y + row * N;
@@ -162,11 +195,12 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
             for (int k = 0; k < IT; ++k) {
                 const int v = lane + k * tpr;
                 if (v < nv) {
-                    float wf[V], bf[V], o[V];
+                    float f[V], wf[V], bf[V], o[V];
+                    VT::unpack(xr[k], f);
                     VT::unpack(wr[k], wf);
                     VT::unpack(br[k], bf);
 #pragma unroll
-                    for (int e = 0; e < V; ++e) o[e] = (xf[k][e] - mean) * rstd * wf[e] + bf[e];
+                    for (int e = 0; e < V; ++e) o[e] = (f[e] - mean) * rstd * wf[e] + bf[e];
                     vstore_stream<T, V>(yrow + (int64_t)v * V, VT::pack(o));
                 }
             }
@@ -175,6 +209,8 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
                 if (rstd_out) rstd_out[row] = rstd;
             }
         }
+#pragma unroll
+        for (int k = 0; k < IT; ++k) xr[k] = nx[k];
     }
 }
 
@@ -213,64 +249,111 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
 #pragma unroll
         for (int e = 0; e < V; ++e) acc_w[k][e] = acc_b[k][e] = 0.0f;
 
+    // Software pipelined: the next row's x, dy and statistics are loaded
+    // before this row is reduced and written.
     int slot = 0;
-    for (int64_t base = (int64_t)blockIdx.x * rpb; base < M; base += (int64_t)gridDim.x * rpb) {
+    const int64_t step = (int64_t)gridDim.x * rpb;
+    int64_t base = (int64_t)blockIdx.x * rpb;
+    raw_t rx[IT], rd[IT];
+    float mean = 0.0f, rstd = 0.0f;
+    {
         const int64_t row = base + slot_in_block;
-        const bool active = row < M;
-
-        float xf[IT][V], gf[IT][V];
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const int v = lane + k * tpr;
-            raw_t rx = zeros_raw<VT>(), rd = zeros_raw<VT>();
-            if (active && v < nv) {
-                rx = vload_stream<T, V>(x + row * N + (int64_t)v * V);
-                rd = vload_stream<T, V>(dy + row * N + (int64_t)v * V);
+            rx[k] = zeros_raw<VT>();
+            rd[k] = zeros_raw<VT>();
+            if (row < M && v < nv) {
+                rx[k] = vload_stream<T, V>(x + row * N + (int64_t)v * V);
+                rd[k] = vload_stream<T, V>(dy + row * N + (int64_t)v * V);
             }
-            VT::unpack(rx, xf[k]);
-            VT::unpack(rd, gf[k]);  // dy for now; g after the weight product
         }
-        const float mean = (!RMS && active) ? mean_in[row] : 0.0f;
-        const float rstd = active ? rstd_in[row] : 0.0f;
+        if (row < M) {
+            if (!RMS) mean = mean_in[row];
+            rstd = rstd_in[row];
+        }
+    }
+    for (; base < M; base += step) {
+        const int64_t row = base + slot_in_block;
+        const bool active = row < M;
+        const int64_t nrow = row + step;
+        raw_t nx[IT], nd[IT];
+        float nmean = 0.0f, nrstd = 0.0f;
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int v = lane + k * tpr;
+            nx[k] = zeros_raw<VT>();
+            nd[k] = zeros_raw<VT>();
+            if (nrow < M && v < nv) {
+                nx[k] = vload_stream<T, V>(x + nrow * N + (int64_t)v * V);
+                nd[k] = vload_stream<T, V>(dy + nrow * N + (int64_t)v * V);
+            }
+        }
+        if (nrow < M) {
+            if (!RMS) nmean = mean_in[nrow];
+            nrstd = rstd_in[nrow];
+        }
+#pragma unroll
+        for (int k = 0; k < IT; ++k) opaque(wr[k]);  // keep w packed (no hoisted float copy)
 
+        // Pass 1: the row sums and the column partials.  Out-of-range
+        // elements hold x = dy = 0 and add nothing (their g is 0).
         float s_gx = 0.0f, s_g = 0.0f;
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
-            float wf[V];
+            float xf[V], df[V], wf[V];
+            VT::unpack(rx[k], xf);
+            VT::unpack(rd[k], df);
             VT::unpack(wr[k], wf);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                const float d = gf[k][e];
-                const float xh = (xf[k][e] - mean) * rstd;
-                acc_w[k][e] += d * xh;
-                if (!RMS) acc_b[k][e] += d;
-                const float g = d * wf[e];
-                xf[k][e] = xh;
-                gf[k][e] = g;
-                s_gx += g * xh;
+                const float xh = (xf[e] - mean) * rstd;
+                acc_w[k][e] = fmaf(df[e], xh, acc_w[k][e]);
+                if (!RMS) acc_b[k][e] += df[e];
+                const float g = df[e] * wf[e];
+                s_gx = fmaf(g, xh, s_gx);
                 s_g += g;
             }
         }
-        // Out-of-range elements hold x = dy = 0, so they add nothing above;
-        // for LayerNorm xhat of a padded element is -mean*rstd but its g is 0.
         if (RMS) s_g = 0.0f;
         row_sum2(s_gx, s_g, tpr, lds, slot);
         slot ^= 1;
         const float c_gx = s_gx * inv_n, c_g = s_g * inv_n;
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            opaque(rx[k]);
+            opaque(rd[k]);
+            opaque(wr[k]);
+        }
 
+        // Pass 2: dx from the packed row.
         if (active) {
             T *dxrow = dx + row * N;
 #pragma unroll
             for (int k = 0; k < IT; ++k) {
                 const int v = lane + k * tpr;
                 if (v < nv) {
-                    float o[V];
+                    float xf[V], df[V], wf[V], o[V];
+                    VT::unpack(rx[k], xf);
+                    VT::unpack(rd[k], df);
+                    VT::unpack(wr[k], wf);
 #pragma unroll
-                    for (int e = 0; e < V; ++e) o[e] = rstd * (gf[k][e] - c_g - xf[k][e] * c_gx);
+                    for (int e = 0; e < V; ++e) {
+                        const float xh = (xf[e] - mean) * rstd;
+                        const float g = df[e] * wf[e];
+                        o[e] = rstd * (g - c_g - xh * c_gx);
+                    }
                     vstore_stream<T, V>(dxrow + (int64_t)v * V, VT::pack(o));
                 }
             }
         }
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            rx[k] = nx[k];
+            rd[k] = nd[k];
+        }
+        mean = nmean;
+        rstd = nrstd;
     }
 
     // Combine the row slots of this block column by column and write one
@@ -291,54 +374,64 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
         }
         return;
     }
-    extern __shared__ float colbuf[];  // blockDim.x * V floats
+    // Several row slots: stage every slot's column partials in LDS as
+    // [slot][column], then let all threads add over the slots (in slot
+    // order) for their own columns and write the block's partial row.
+    extern __shared__ float colbuf[];  // rpb * N floats
     for (int which = 0; which < 2; ++which) {
         float *part = which == 0 ? part_w : part_b;
         if (part == nullptr) continue;
+        __syncthreads();
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const int v = lane + k * tpr;
-            __syncthreads();
+            if (v < nv) {
 #pragma unroll
-            for (int e = 0; e < V; ++e)
-                colbuf[e * blockDim.x + threadIdx.x] = which == 0 ? acc_w[k][e] : acc_b[k][e];
-            __syncthreads();
-            if (slot_in_block == 0 && v < nv) {
-                float o[V];
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    float s = 0.0f;
-                    for (int r = 0; r < rpb; ++r) s += colbuf[e * blockDim.x + r * tpr + threadIdx.x];
-                    o[e] = s;
-                }
-                float *dst = part + (int64_t)blockIdx.x * N + (int64_t)v * V;
-#pragma unroll
-                for (int e = 0; e < V; ++e) dst[e] = o[e];
+                for (int e = 0; e < V; ++e)
+                    colbuf[slot_in_block * N + v * V + e] = which == 0 ? acc_w[k][e] : acc_b[k][e];
             }
+        }
+        __syncthreads();
+        for (int col = threadIdx.x; col < N; col += blockDim.x) {
+            float sum = 0.0f;
+            for (int r = 0; r < rpb; ++r) sum += colbuf[r * N + col];
+            part[(int64_t)blockIdx.x * N + col] = sum;
         }
     }
 }
 
 // Column sums of G partial rows (float64, fixed order) -> dw / db in T.
-// blockDim = (64, 4): 64 columns per block, 4 interleaved row groups.
+// blockDim = (16 columns, 16 row slices); grid = (ceil(N/16), 1 or 2).
+// Each thread adds rows slice, slice+16, ... with eight loads in flight,
+// then the 16 slices are added in order through LDS.
+constexpr int kColsumCols = 16;
+constexpr int kColsumSlices = 16;
 template <typename T>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kColsumCols * kColsumSlices)
 colsum_kernel(const float *__restrict__ part_w, const float *__restrict__ part_b, int G, int N,
               T *__restrict__ dw, T *__restrict__ db) {
-    __shared__ double red[4][64];
+    __shared__ double red[kColsumSlices][kColsumCols];
     const float *part = blockIdx.y == 0 ? part_w : part_b;
     T *out = blockIdx.y == 0 ? dw : db;
     if (part == nullptr || out == nullptr) return;  // uniform per block
-    const int col = blockIdx.x * 64 + threadIdx.x;
+    const int col = blockIdx.x * kColsumCols + threadIdx.x;
     double s = 0.0;
-    if (col < N)
-        for (int g = threadIdx.y; g < G; g += 4) s += (double)part[(int64_t)g * N + col];
+    if (col < N) {
+        int g = threadIdx.y;
+        for (; g + 7 * kColsumSlices < G; g += 8 * kColsumSlices) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(g + u * kColsumSlices) * N + col];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += (double)v[u];
+        }
+        for (; g < G; g += kColsumSlices) s += (double)part[(int64_t)g * N + col];
+    }
     red[threadIdx.y][threadIdx.x] = s;
     __syncthreads();
     if (threadIdx.y == 0 && col < N) {
-        double t = red[0][threadIdx.x] + red[1][threadIdx.x];
-        t += red[2][threadIdx.x];
-        t += red[3][threadIdx.x];
+        double t = 0.0;
+        for (int i = 0; i < kColsumSlices; ++i) t += red[i][threadIdx.x];
         st1(out + col, (float)t);
     }
 }
@@ -382,18 +475,27 @@ static bool make_plan(norm_dtype dt, int64_t M, int64_t N, bool vec_ok, bool bac
     int best_tpr = -1, best_it = -1;
     int64_t best_waste = INT64_MAX;
     // Smallest idle-slot count; ties go to more vectors per thread (fewer,
-    // longer-running threads keep more loads in flight per thread).
-    for (int tpr = 1; tpr <= 1024; tpr *= 2) {
-        for (int i = 0; i < n_its; ++i) {
-            const int it = its[i];
-            if ((int64_t)tpr * it < nv) continue;
-            const int64_t waste = (int64_t)tpr * it - nv;
-            if (waste < best_waste || (waste == best_waste && it > best_it)) {
-                best_waste = waste; best_tpr = tpr; best_it = it;
+    // longer-running threads).  Vectors per thread are capped at 4 (16 for
+    // the scalar path) while any tiling fits: holding more of the row costs
+    // more registers than it buys (measured on the RMSNorm 16384 x 4096 and
+    // ViT LayerNorm shapes).
+    const int it_cap = vec_ok ? 4 : 16;
+    for (int pass = 0; pass < 2 && best_tpr < 0; ++pass) {
+        for (int tpr = 1; tpr <= 1024; tpr *= 2) {
+            for (int i = 0; i < n_its; ++i) {
+                const int it = its[i];
+                if (pass == 0 && it > it_cap) continue;
+                if ((int64_t)tpr * it < nv) continue;
+                const int64_t waste = (int64_t)tpr * it - nv;
+                if (waste < best_waste || (waste == best_waste && it > best_it)) {
+                    best_waste = waste; best_tpr = tpr; best_it = it;
+                }
             }
         }
     }
     if (best_tpr < 0) return false;
+    // Persistent blocks per CU: the forward keeps 4 (16 waves) resident; the
+    // backward 2, because every block adds a partial row for dw / db.
     int bpc = backward ? 2 : 4;
     int otpr, oit, obpc;
     if (env_override(&otpr, &oit, &obpc) && otpr >= 1 && otpr <= 1024 && (otpr & (otpr - 1)) == 0 &&
@@ -440,10 +542,8 @@ static norm_status launch_fwd_v(const RowPlan &p, hipStream_t s, const void *x, 
     case 64: if constexpr (V == 1) fn = p.block > 256 ? row_fwd_kernel<T, V, 64, RMS, 1024> : row_fwd_kernel<T, V, 64, RMS, 256>; break;
     }
     if (!fn) return NORM_ERR_SHAPE;
-    hook_before(s, RMS ? "row_fwd_kernel<rms>" : "row_fwd_kernel<ln>");
-    hipLaunchKernelGGL(fn, dim3(p.grid), dim3(p.block), 0, s, (const T *)x, (const T *)w,
-                       (const T *)b, (T *)y, mean, rstd, M, N, 1.0f / (float)N, eps, p.tpr);
-    hook_after(s);
+    launch(RMS ? "row_fwd_kernel<rms>" : "row_fwd_kernel<ln>", true, fn, dim3(p.grid), dim3(p.block), 0, s,
+           (const T *)x, (const T *)w, (const T *)b, (T *)y, mean, rstd, M, N, 1.0f / (float)N, eps, p.tpr);
     return launch_status();
 }
 
@@ -466,12 +566,11 @@ static norm_status launch_bwd_v(const RowPlan &p, hipStream_t s, const void *dy,
     case 64: if constexpr (V == 1) fn = p.block > 256 ? row_bwd_kernel<T, V, 64, RMS, 1024> : row_bwd_kernel<T, V, 64, RMS, 256>; break;
     }
     if (!fn) return NORM_ERR_SHAPE;
-    const size_t shmem = (part_w || part_b) ? (size_t)p.block * V * sizeof(float) : 0;
-    hook_before(s, RMS ? "row_bwd_kernel<rms>" : "row_bwd_kernel<ln>");
-    hipLaunchKernelGGL(fn, dim3(p.grid), dim3(p.block), shmem, s, (const T *)dy, (const T *)x,
-                       (const T *)w, mean, rstd, (T *)dx, part_w, part_b, M, N,
-                       1.0f / (float)N, p.tpr);
-    hook_after(s);
+    const int rpb = p.block / p.tpr;
+    const size_t shmem = ((part_w || part_b) && rpb > 1) ? (size_t)rpb * N * sizeof(float) : 0;
+    launch(RMS ? "row_bwd_kernel<rms>" : "row_bwd_kernel<ln>", true, fn, dim3(p.grid), dim3(p.block), shmem, s,
+           (const T *)dy, (const T *)x, (const T *)w, mean, rstd, (T *)dx, part_w, part_b, M, N,
+           1.0f / (float)N, p.tpr);
     return launch_status();
 }
 
@@ -494,6 +593,7 @@ template <bool RMS>
 static norm_status fwd_entry(norm_dtype dt, int64_t M, int64_t N, float eps, const void *x,
                              const void *w, const void *b, void *y, float *mean, float *rstd,
                              void *stream) {
+    CallScope scope;
     norm_status st = check_rows(dt, M, N);
     if (st != NORM_OK) return st;
     if (!(eps >= 0.0f)) return NORM_ERR_ARG;
@@ -520,6 +620,7 @@ template <bool RMS>
 static norm_status bwd_entry(norm_dtype dt, int64_t M, int64_t N, const void *dy, const void *x,
                              const void *w, const float *mean, const float *rstd, void *dx,
                              void *dw, void *db, void *ws, size_t ws_bytes, void *stream) {
+    CallScope scope;
     norm_status st = check_rows(dt, M, N);
     if (st != NORM_OK) return st;
     if (!dy || !x || !rstd || !dx || (!RMS && !mean)) {
@@ -538,9 +639,9 @@ static norm_status bwd_entry(norm_dtype dt, int64_t M, int64_t N, const void *dy
         for (void *out : {dw, db}) {
             if (!out) continue;
             if (dt == NORM_F32)
-                hipLaunchKernelGGL(zero_fill_kernel<float>, grid, dim3(256), 0, s, (float *)out, n);
+                launch("zero_fill_kernel", false, zero_fill_kernel<float>, grid, dim3(256), 0, s, (float *)out, n);
             else
-                hipLaunchKernelGGL(zero_fill_kernel<bf16_t>, grid, dim3(256), 0, s, (bf16_t *)out, n);
+                launch("zero_fill_kernel", false, zero_fill_kernel<bf16_t>, grid, dim3(256), 0, s, (bf16_t *)out, n);
         }
         return launch_status();
     }
@@ -556,13 +657,14 @@ static norm_status bwd_entry(norm_dtype dt, int64_t M, int64_t N, const void *dy
         st = vec ? launch_bwd_v<bf16_t, RMS, 8>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n)
                  : launch_bwd_v<bf16_t, RMS, 1>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n);
     if (st != NORM_OK || !want) return st;
-    dim3 grid((unsigned)ceil_div(N, 64), RMS ? 1 : 2);
+    dim3 grid((unsigned)ceil_div(N, kColsumCols), RMS ? 1 : 2);
+    dim3 block(kColsumCols, kColsumSlices);
     if (dt == NORM_F32)
-        hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(64, 4), 0, s, part_w, part_b, p.grid, n,
-                           (float *)dw, (float *)db);
+        launch("colsum_kernel", false, colsum_kernel<float>, grid, block, 0, s, (const float *)part_w,
+               (const float *)part_b, p.grid, n, (float *)dw, (float *)db);
     else
-        hipLaunchKernelGGL(colsum_kernel<bf16_t>, grid, dim3(64, 4), 0, s, part_w, part_b, p.grid, n,
-                           (bf16_t *)dw, (bf16_t *)db);
+        launch("colsum_kernel", false, colsum_kernel<bf16_t>, grid, block, 0, s, (const float *)part_w,
+               (const float *)part_b, p.grid, n, (bf16_t *)dw, (bf16_t *)db);
     return launch_status();
 }
 

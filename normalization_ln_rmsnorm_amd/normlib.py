@@ -43,8 +43,10 @@ SIGNATURES = {
     "bn_bwd": (_I, [_I, _I64, _I64, _I64, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
                     _SZ, _V]),
     "norm_status_str": (ctypes.c_char_p, [_I]),
-    "norm_arm_kernel_events": (None, [_V, _V]),
-    "norm_last_kernel_name": (ctypes.c_char_p, []),
+    "norm_arm_kernel_events": (None, [ctypes.POINTER(ctypes.c_void_p), _I]),
+    "norm_last_kernel_count": (_I, []),
+    "norm_last_kernel_name": (ctypes.c_char_p, [_I]),
+    "norm_last_main_kernel": (_I, []),
 }
 
 _lib = None
@@ -124,13 +126,17 @@ def _workspace(nbytes, device, ws):
     return ws, ws.numel() * ws.element_size()
 
 
-def arm_kernel_events(start, stop):
-    """Arm two hipEvent_t handles (ints) around the next call's main kernel."""
-    lib().norm_arm_kernel_events(start, stop)
+def arm_kernel_events(events):
+    """Arm hipEvent_t handles for the next call: kernel i of that call is
+    launched with events[2i] / events[2i+1] attached to its dispatch."""
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(getattr(e, "value", e)) for e in events])
+    lib().norm_arm_kernel_events(arr, len(events) // 2)
 
 
-def last_kernel_name():
-    return lib().norm_last_kernel_name().decode()
+def last_kernels():
+    """(names of the kernels the last call launched, index of its main kernel)."""
+    n = lib().norm_last_kernel_count()
+    return [lib().norm_last_kernel_name(i).decode() for i in range(n)], lib().norm_last_main_kernel()
 
 
 # ---------------------------------------------------------------- LayerNorm

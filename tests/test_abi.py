@@ -37,7 +37,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["ln_fwd", "ln_bwd", "ln_bwd_workspace_bytes", "rms_fwd", "rms_bwd",
               "rms_bwd_workspace_bytes", "bn_workspace_bytes", "bn_fwd_train", "bn_fwd_eval",
-              "bn_bwd", "norm_status_str", "norm_arm_kernel_events", "norm_last_kernel_name"]:
+              "bn_bwd", "norm_status_str", "norm_arm_kernel_events", "norm_last_kernel_count",
+              "norm_last_kernel_name", "norm_last_main_kernel"]:
         assert n in names, n
 
 
@@ -132,3 +133,14 @@ def test_workspace_sizes_scale(lib):
     big = lib.bn_workspace_bytes(BF16, 256, 64, 12544)
     assert 0 < small < 1 << 22 and 0 < big < 1 << 22
     assert lib.rms_bwd_workspace_bytes(BF16, 16384, 4096) <= 64 << 20
+
+
+def test_timing_hook_bookkeeping_without_gpu(lib):
+    """A call that fails validation launches nothing and disarms the hook."""
+    ev = (ctypes.c_void_p * 2)(None, None)
+    lib.norm_arm_kernel_events(ev, 1)
+    assert lib.ln_fwd(F32, 4, 0, 1e-5, P, NULL, NULL, P, NULL, NULL, NULL) == ESHAPE
+    assert lib.norm_last_kernel_count() == 0
+    assert lib.norm_last_main_kernel() == -1
+    assert lib.norm_last_kernel_name(0) == b""
+    lib.norm_arm_kernel_events(None, 0)
