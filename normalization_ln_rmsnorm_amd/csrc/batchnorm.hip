@@ -27,9 +27,10 @@
 //                       float64 triple per tile ([NormPage] "BatchNorm":
 //                       online correction by the difference from the previous
 //                       mean, no second pass; [MathPage] "Practice 2").
-//     bn_apply_kernel   each workgroup first merges its channel's tile
-//                       triples (float64, fixed order: every workgroup of a
-//                       channel gets the same bits), the channel's first
+//     bn_apply_kernel   each workgroup first combines its channel's tile
+//                       triples (float64, exact parallel-axis identity, fixed
+//                       order: every workgroup of a channel gets the same
+//                       bits), the channel's first
 //                       workgroup saves mean / rstd and applies the momentum
 //                       update, then z = x * a_c + s_c (+ res), y = act(z)
 //                       with a_c = w_c * rstd_c, s_c = b_c - mean_c * a_c.
@@ -199,24 +200,32 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, double *__restrict__ part) {
 }
 
 // ------------------------------------------- forward: channel statistics
-// Merges channel c's tile triples in float64 on the block's first wave
-// (lane-strided, then a butterfly of the symmetric merge) and shares the
-// result through LDS.  The order is fixed, so every workgroup of channel c
-// obtains the same bits.
+// Combines channel c's tile triples (n_t, mean_t, M2_t) in float64 on the
+// block's first wave with the exact parallel-axis identity
+//   mean = sum n_t mean_t / n,   M2 = sum [M2_t + n_t (mean_t - mean)^2],
+// two butterfly sums and one division (a chain of pairwise merges would
+// need a division per step, and every workgroup of the channel repeats
+// this).  The order is fixed, so every workgroup of channel c obtains the
+// same bits; the result is shared through LDS.
 __device__ __forceinline__ WelfD merge_channel_tiles(const double *__restrict__ part, int c, int tiles) {
     __shared__ WelfD sh;
     if (threadIdx.x < kWave) {
-        WelfD acc{0.0, 0.0, 0.0};
+        const double *q = part + (int64_t)c * tiles * 3;
+        double sn = 0.0, snm = 0.0;
         for (int t = threadIdx.x; t < tiles; t += kWave) {
-            const double *q = part + ((int64_t)c * tiles + t) * 3;
-            acc = welf_merge(acc, WelfD{q[0], q[1], q[2]});
+            sn += q[t * 3 + 0];
+            snm = fma(q[t * 3 + 0], q[t * 3 + 1], snm);
         }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            WelfD o{shfl_xor_d(acc.n, m), shfl_xor_d(acc.mean, m), shfl_xor_d(acc.m2, m)};
-            acc = welf_merge(acc, o);
+        sn = wave_sum_d(sn);
+        snm = wave_sum_d(snm);
+        const double mean = snm / sn;
+        double m2 = 0.0;
+        for (int t = threadIdx.x; t < tiles; t += kWave) {
+            const double d = q[t * 3 + 1] - mean;
+            m2 += fma(q[t * 3 + 0] * d, d, q[t * 3 + 2]);
         }
-        if (threadIdx.x == 0) sh = acc;
+        m2 = wave_sum_d(m2);
+        if (threadIdx.x == 0) sh = WelfD{sn, mean, m2};
     }
     __syncthreads();
     return sh;
@@ -311,15 +320,18 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
     bn_coeffs(mean, save_rstd[c], w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a, &s);
     const int64_t nvp = g.HW / V;
 
-    // Per-element accumulation type: float64 for float32 I/O (x - mean and
-    // dz * (x - mean) are then exact, which the 1e-5 tolerance on the
-    // channel sums needs when a channel's dw lands near zero), float32 per
-    // thread for bf16 I/O (ample for bf16 outputs).  Threads and tiles are
-    // always combined in float64.  The third sum, of x - mean, corrects for
-    // the saved mean being rounded to float32.
-    using Acc = typename std::conditional<sizeof(T) == 4, double, float>::type;
+    // Accumulation.  Float32 I/O: float64 per element, so x - mean and
+    // dz * (x - mean) are exact -- the 1e-5 tolerance on the channel sums
+    // needs it when a channel's dw lands near zero -- plus the sum of
+    // x - mean, which corrects for the saved mean being rounded to float32.
+    // bf16 I/O: float32 per thread of dz and dz * x (the mean is taken out
+    // once per tile in float64); ample for bf16 outputs and two VALU
+    // operations per element cheaper where the GELU backward is VALU-bound.
+    // Threads and tiles are always combined in float64.
+    constexpr bool kExact = sizeof(T) == 4;
+    using Acc = typename std::conditional<kExact, double, float>::type;
     Acc s_dz = 0, s_dzx = 0, s_xc = 0;
-    const Acc mean_a = (Acc)mean;
+    const Acc mean_a = kExact ? (Acc)mean : (Acc)0;
     for (int64_t n = n0; n < n1; ++n) {
         const int64_t off = plane_offset(g, n, c);
         for (int64_t v0 = threadIdx.x; v0 < nvp; v0 += (int64_t)kBnBlock * kBnUnroll) {
@@ -346,15 +358,15 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
                         if (ACT != kActNone) {
                             float z = fmaf(xf[e], a, s);
                             if (RES) z += rf[e];
-                            dz[e] = df[e] * act_grad<ACT, sizeof(T) == 2>(z);
+                            dz[e] = df[e] * act_grad<ACT, !kExact>(z);
                         } else {
                             dz[e] = df[e];
                         }
-                        const Acc xc = (Acc)xf[e] - mean_a;
+                        const Acc xc = kExact ? (Acc)xf[e] - mean_a : (Acc)xf[e];
                         const Acc d = (Acc)dz[e];
                         s_dz += d;
                         s_dzx = fma(d, xc, s_dzx);
-                        s_xc += xc;
+                        if (kExact) s_xc += xc;
                     }
                     if (RES) vstore_stream<T, V>(dres + off + v * V, VT::pack(dz));
                 }
@@ -379,6 +391,7 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
             p1 += wave_part[i][1];
             p2 += wave_part[i][2];
         }
+        if (!kExact) p1 -= (double)mean * p0;  // sum dz * x  ->  sum dz * (x - mean)
         double *dst = part + ((int64_t)c * g.tiles + blockIdx.x / (unsigned)g.C) * 3;
         dst[0] = p0;
         dst[1] = p1;
@@ -454,6 +467,9 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
     const double k2d = -wc * r * r * dgamma / n_total;
     const float k1 = (float)(wc * r), k2 = (float)k2d;
     const float k3 = (float)(-wc * r * dbeta / n_total - k2d * mean_shift);
+    // bf16 I/O: fold the mean into the constant, dx = k1 dz + k2 x + k3m.
+    constexpr bool kExact = sizeof(T) == 4;
+    const float k3m = (float)(-wc * r * dbeta / n_total - k2d * mean_shift - k2d * (double)mean);
     float a = 0.0f, s = 0.0f;
     if (DZ_SRC == 2) bn_coeffs(mean, rstd_f, wc_f, b ? ld1(b + c) : 0.0f, &a, &s);
     const int64_t nvp = g.HW / V;
@@ -488,7 +504,7 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
                             if (RES) z += rf[e];
                             dz = df[e] * act_grad<ACT, kFast>(z);
                         }
-                        o[e] = fmaf(k1, dz, fmaf(k2, xf[e] - mean, k3));
+                        o[e] = kExact ? fmaf(k1, dz, fmaf(k2, xf[e] - mean, k3)) : fmaf(k1, dz, fmaf(k2, xf[e], k3m));
                     }
                     vstore_stream<T, V>(dx + off + v * V, VT::pack(o));
                 }

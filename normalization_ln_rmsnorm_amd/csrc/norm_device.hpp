@@ -179,7 +179,8 @@ __device__ __forceinline__ double shfl_xor_d(double v, int mask) {
 //    needs, so Phi and phi share one exp; in float32 the result is within
 //    3e-7 of Phi (and of GELU') everywhere -- far inside 2 bf16 ulp.
 //    The coefficients below are A&S's a1..a5 halved (they give Phi(-|z|)
-//    = erfc(u) / 2 directly).
+//    = erfc(u) / 2 directly).  This form serves the derivative, which needs
+//    both Phi and phi; the forward uses the cheaper gelu_fast below.
 enum Act : int { kActNone = 0, kActRelu = 1, kActGelu = 2 };
 
 constexpr float kInvSqrt2 = 0.70710678118654752440f;
@@ -207,10 +208,33 @@ template <bool FAST> __device__ __forceinline__ NormalPdfCdf normal_pdf_cdf(floa
     }
 }
 
+// Fast forward GELU (FAST = true).  The forward needs Phi but not phi, so it
+// uses Abramowitz & Stegun eq. 7.1.28, erf(u) ~= 1 - 1 / (1 + a1 u + ... +
+// a6 u^6)^16 for u >= 0, |error| <= 3e-7, which costs one reciprocal and no
+// exp.  With r16 = (1 + a1 u + ... + a6 u^6)^-16 and u = |z| / sqrt 2,
+// z * Phi(z) = max(z, 0) - |z| * r16 / 2 for either sign of z.  In float32
+// the result is within 7.1e-7 of GELU(z) (below 0.04 bf16 ulp wherever
+// |GELU(z)| > 2^-10).
+__device__ __forceinline__ float gelu_fast(float z) {
+    const float u = fabsf(z) * kInvSqrt2;
+    float p = fmaf(0.0000430638f, u, 0.0002765672f);
+    p = fmaf(p, u, 0.0001520143f);
+    p = fmaf(p, u, 0.0092705272f);
+    p = fmaf(p, u, 0.0422820123f);
+    p = fmaf(p, u, 0.0705230784f);
+    p = fmaf(p, u, 1.0f);
+    float r = __builtin_amdgcn_rcpf(p);
+    r *= r;
+    r *= r;
+    r *= r;
+    r *= r;  // r = p^-16
+    return fmaf(-0.5f * fabsf(z), r, fmaxf(z, 0.0f));
+}
+
 template <int ACT, bool FAST = false> __device__ __forceinline__ float act_fwd(float z) {
     if constexpr (ACT == kActRelu) return z > 0.0f ? z : 0.0f;
     else if constexpr (ACT == kActGelu) {
-        if constexpr (FAST) return z * normal_pdf_cdf<true>(z).Phi;
+        if constexpr (FAST) return gelu_fast(z);
         else return 0.5f * z * (1.0f + erff(z * kInvSqrt2));
     } else return z;
 }
