@@ -64,10 +64,27 @@ typedef enum {
 
 typedef enum { NORM_F32 = 0, NORM_BF16 = 1 } norm_dtype;
 
-/* Activation fused after BatchNorm ([ActPage] sections 5-6; [NormPage]
- * "BatchNorm" section): none, ReLU (derivative 0 at z <= 0), or the exact
- * error-function GELU, z * Phi(z). */
-typedef enum { NORM_ACT_NONE = 0, NORM_ACT_RELU = 1, NORM_ACT_GELU = 2 } norm_act;
+/* Activation fused after BatchNorm ([NormPage] "BatchNorm" section: relu,
+ * gelu, silu, mish, leaky_relu and a dozen more; [ActPage] sections 5-6).
+ * Definitions and derivative conventions at kinks are PyTorch's:
+ *   RELU        max(z,0), derivative 0 at z <= 0
+ *   GELU        exact error-function form z * Phi(z)
+ *   SIGMOID, TANH, SILU (z * sigmoid z), MISH (z * tanh(softplus z)),
+ *   LEAKY_RELU  z > 0 ? z : p * z                 (p = negative slope)
+ *   ELU         z > 0 ? z : p * (e^z - 1)          (p = alpha)
+ *   SELU        1.0507 * (z > 0 ? z : 1.6733 (e^z - 1))
+ *   CELU        z > 0 ? z : p * (e^(z/p) - 1)      (p = alpha, nonzero)
+ *   SOFTPLUS    log(1 + e^z), z above 20 passes through
+ *   RELU6       min(max(z,0),6); HARDSIGMOID relu6(z+3)/6;
+ *   HARDSWISH   z * relu6(z+3)/6
+ * `act_param` (the p above) is ignored by the others.  NONE, RELU and GELU
+ * have specialized kernels; the rest share a run-time-dispatched one. */
+typedef enum {
+    NORM_ACT_NONE = 0, NORM_ACT_RELU = 1, NORM_ACT_GELU = 2, NORM_ACT_SIGMOID = 3,
+    NORM_ACT_TANH = 4, NORM_ACT_SILU = 5, NORM_ACT_MISH = 6, NORM_ACT_LEAKY_RELU = 7,
+    NORM_ACT_ELU = 8, NORM_ACT_SELU = 9, NORM_ACT_CELU = 10, NORM_ACT_SOFTPLUS = 11,
+    NORM_ACT_RELU6 = 12, NORM_ACT_HARDSIGMOID = 13, NORM_ACT_HARDSWISH = 14
+} norm_act;
 
 /* Largest row width the row-wise kernels accept (rows are held in
  * registers): 65536 features for bf16, 32768 for float32. */
@@ -146,10 +163,11 @@ size_t bn_workspace_bytes(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW);
  *   running_mean/var      nullable float32 [C], updated in place
  *   save_mean, save_rstd  required float32 [C] outputs (for bn_bwd)
  *   ws                    bn_workspace_bytes(dt, Nb, C, HW) bytes
- * Requires Nb*HW >= 2, eps >= 0, 0 <= momentum <= 1.                    */
+ * Requires Nb*HW >= 2, eps >= 0, 0 <= momentum <= 1, a finite act_param
+ * (nonzero for CELU).                                                     */
 norm_status bn_fwd_train(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW,
                          float eps, float momentum, norm_act act,
-                         const void *x, const void *res, const void *w,
+                         float act_param, const void *x, const void *res, const void *w,
                          const void *b, float *running_mean,
                          float *running_var, float *save_mean,
                          float *save_rstd, void *y, void *ws,
@@ -159,7 +177,7 @@ norm_status bn_fwd_train(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW,
  * running statistics): z = (x - rm_c) / sqrt(rv_c + eps) * w_c + b_c
  * (+ res), y = act(z).  running_mean/var required; res, w, b nullable.   */
 norm_status bn_fwd_eval(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW,
-                        float eps, norm_act act, const void *x,
+                        float eps, norm_act act, float act_param, const void *x,
                         const void *res, const void *w, const void *b,
                         const float *running_mean, const float *running_var,
                         void *y, void *stream);
@@ -176,7 +194,7 @@ norm_status bn_fwd_eval(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW,
  *   save_mean/rstd required (from bn_fwd_train)
  *   ws             bn_workspace_bytes(dt, Nb, C, HW) bytes.              */
 norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW,
-                   norm_act act, const void *dy, const void *x,
+                   norm_act act, float act_param, const void *dy, const void *x,
                    const void *res, const void *w, const void *b,
                    const float *save_mean, const float *save_rstd, void *dx,
                    void *dres, void *dw, void *db, void *ws, size_t ws_bytes,

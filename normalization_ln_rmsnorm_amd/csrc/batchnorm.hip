@@ -245,7 +245,7 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
                 const T *__restrict__ b, const double *__restrict__ part, float eps, float momentum,
                 float *__restrict__ running_mean, float *__restrict__ running_var,
                 float *__restrict__ save_mean, float *__restrict__ save_rstd, T *__restrict__ y,
-                BnGeom g) {
+                BnGeom g, int act_rt, float act_p) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
     constexpr bool kFast = sizeof(T) == 2;
@@ -295,7 +295,7 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
                     for (int e = 0; e < V; ++e) {
                         float z = fmaf(f[e], a, s);
                         if (RES) z += rf[e];
-                        o[e] = act_fwd<ACT, kFast>(z);
+                        o[e] = act_fwd_any<ACT, kFast>(z, act_rt, act_p);
                     }
                     vstore_stream<T, V>(y + off + v * V, VT::pack(o));
                 }
@@ -310,7 +310,8 @@ __global__ void __launch_bounds__(kBnBlock)
 bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__restrict__ res,
                      const T *__restrict__ w, const T *__restrict__ b,
                      const float *__restrict__ save_mean, const float *__restrict__ save_rstd,
-                     T *__restrict__ dres, BnGeom g, double *__restrict__ part) {
+                     T *__restrict__ dres, BnGeom g, double *__restrict__ part, int act_rt,
+                     float act_p) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
     int c; int64_t n0, n1;
@@ -358,7 +359,7 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
                         if (ACT != kActNone) {
                             float z = fmaf(xf[e], a, s);
                             if (RES) z += rf[e];
-                            dz[e] = df[e] * act_grad<ACT, !kExact>(z);
+                            dz[e] = df[e] * act_grad_any<ACT, !kExact>(z, act_rt, act_p);
                         } else {
                             dz[e] = df[e];
                         }
@@ -445,7 +446,7 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
                  const T *__restrict__ dres, const T *__restrict__ w, const T *__restrict__ b,
                  const float *__restrict__ save_mean, const float *__restrict__ save_rstd,
                  const double *__restrict__ part, double n_total, T *__restrict__ dw, T *__restrict__ db,
-                 T *__restrict__ dx, BnGeom g) {
+                 T *__restrict__ dx, BnGeom g, int act_rt, float act_p) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
     constexpr bool kFast = sizeof(T) == 2;
@@ -502,7 +503,7 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
                         if (DZ_SRC == 2 && ACT != kActNone) {
                             float z = fmaf(xf[e], a, s);
                             if (RES) z += rf[e];
-                            dz = df[e] * act_grad<ACT, kFast>(z);
+                            dz = df[e] * act_grad_any<ACT, kFast>(z, act_rt, act_p);
                         }
                         o[e] = kExact ? fmaf(k1, dz, fmaf(k2, xf[e] - mean, k3)) : fmaf(k1, dz, fmaf(k2, xf[e], k3m));
                     }
@@ -563,51 +564,56 @@ static size_t ws_layout(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW) {
 }
 
 template <typename T, int V>
-static norm_status launch_fwd_train(const BnGeom &g, hipStream_t st, norm_act act, float eps, float momentum,
-                                    const void *x, const void *res, const void *w, const void *b,
-                                    float *rm, float *rv, float *sm, float *sr, void *y, void *ws) {
+static norm_status launch_fwd_train(const BnGeom &g, hipStream_t st, norm_act act, float act_p, float eps,
+                                    float momentum, const void *x, const void *res, const void *w,
+                                    const void *b, float *rm, float *rv, float *sm, float *sr, void *y,
+                                    void *ws) {
     const dim3 grid((unsigned)(g.C * (int64_t)g.tiles));
     double *part = static_cast<double *>(ws);
     launch("bn_stats_kernel", false, bn_stats_kernel<T, V>, grid, dim3(kBnBlock), 0, st, (const T *)x, g, part);
     using fn_t = void (*)(const T *, const T *, const T *, const T *, const double *, float, float, float *,
-                          float *, float *, float *, T *, BnGeom);
+                          float *, float *, float *, T *, BnGeom, int, float);
     fn_t fn = nullptr;
     const bool r = res != nullptr;
     switch (act) {
     case NORM_ACT_NONE: fn = r ? bn_apply_kernel<T, V, kActNone, true, 0> : bn_apply_kernel<T, V, kActNone, false, 0>; break;
     case NORM_ACT_RELU: fn = r ? bn_apply_kernel<T, V, kActRelu, true, 0> : bn_apply_kernel<T, V, kActRelu, false, 0>; break;
     case NORM_ACT_GELU: fn = r ? bn_apply_kernel<T, V, kActGelu, true, 0> : bn_apply_kernel<T, V, kActGelu, false, 0>; break;
+    default: fn = r ? bn_apply_kernel<T, V, kActGeneric, true, 0> : bn_apply_kernel<T, V, kActGeneric, false, 0>; break;
     }
     launch("bn_apply_kernel<train>", true, fn, grid, dim3(kBnBlock), 0, st, (const T *)x, (const T *)res,
-           (const T *)w, (const T *)b, (const double *)part, eps, momentum, rm, rv, sm, sr, (T *)y, g);
+           (const T *)w, (const T *)b, (const double *)part, eps, momentum, rm, rv, sm, sr, (T *)y, g, (int)act,
+           act_p);
     return launch_status();
 }
 
 template <typename T, int V>
-static norm_status launch_fwd_eval(const BnGeom &g, hipStream_t st, norm_act act, float eps, const void *x,
-                                   const void *res, const void *w, const void *b, const float *rm,
-                                   const float *rv, void *y) {
+static norm_status launch_fwd_eval(const BnGeom &g, hipStream_t st, norm_act act, float act_p, float eps,
+                                   const void *x, const void *res, const void *w, const void *b,
+                                   const float *rm, const float *rv, void *y) {
     const dim3 grid((unsigned)(g.C * (int64_t)g.tiles));
     using fn_t = void (*)(const T *, const T *, const T *, const T *, const double *, float, float, float *,
-                          float *, float *, float *, T *, BnGeom);
+                          float *, float *, float *, T *, BnGeom, int, float);
     fn_t fn = nullptr;
     const bool r = res != nullptr;
     switch (act) {
     case NORM_ACT_NONE: fn = r ? bn_apply_kernel<T, V, kActNone, true, 1> : bn_apply_kernel<T, V, kActNone, false, 1>; break;
     case NORM_ACT_RELU: fn = r ? bn_apply_kernel<T, V, kActRelu, true, 1> : bn_apply_kernel<T, V, kActRelu, false, 1>; break;
     case NORM_ACT_GELU: fn = r ? bn_apply_kernel<T, V, kActGelu, true, 1> : bn_apply_kernel<T, V, kActGelu, false, 1>; break;
+    default: fn = r ? bn_apply_kernel<T, V, kActGeneric, true, 1> : bn_apply_kernel<T, V, kActGeneric, false, 1>; break;
     }
     // Eval reads the running statistics; they are not written.
     launch("bn_apply_kernel<eval>", true, fn, grid, dim3(kBnBlock), 0, st, (const T *)x, (const T *)res,
            (const T *)w, (const T *)b, (const double *)nullptr, eps, 0.0f, const_cast<float *>(rm),
-           const_cast<float *>(rv), (float *)nullptr, (float *)nullptr, (T *)y, g);
+           const_cast<float *>(rv), (float *)nullptr, (float *)nullptr, (T *)y, g, (int)act, act_p);
     return launch_status();
 }
 
 template <typename T, int V, int ACT>
-static void launch_bwd_act(const BnGeom &g, hipStream_t st, bool has_res, const void *dy, const void *x,
-                           const void *res, const void *w, const void *b, const float *sm, const float *sr,
-                           void *dx, void *dres, void *dw, void *db, void *ws) {
+static void launch_bwd_act(const BnGeom &g, hipStream_t st, bool has_res, int act_rt, float act_p,
+                           const void *dy, const void *x, const void *res, const void *w, const void *b,
+                           const float *sm, const float *sr, void *dx, void *dres, void *dw, void *db,
+                           void *ws) {
     const dim3 grid((unsigned)(g.C * (int64_t)g.tiles));
     const dim3 blk(kBnBlock);
     double *part = static_cast<double *>(ws);
@@ -616,10 +622,12 @@ static void launch_bwd_act(const BnGeom &g, hipStream_t st, bool has_res, const 
     // and writes dres), pass 2 otherwise.
     if (has_res)
         launch("bn_bwd_reduce_kernel", true, bn_bwd_reduce_kernel<T, V, ACT, true>, grid, blk, 0, st,
-               (const T *)dy, (const T *)x, (const T *)res, (const T *)w, (const T *)b, sm, sr, (T *)dres, g, part);
+               (const T *)dy, (const T *)x, (const T *)res, (const T *)w, (const T *)b, sm, sr, (T *)dres, g, part,
+               act_rt, act_p);
     else
         launch("bn_bwd_reduce_kernel", false, bn_bwd_reduce_kernel<T, V, ACT, false>, grid, blk, 0, st,
-               (const T *)dy, (const T *)x, (const T *)res, (const T *)w, (const T *)b, sm, sr, (T *)dres, g, part);
+               (const T *)dy, (const T *)x, (const T *)res, (const T *)w, (const T *)b, sm, sr, (T *)dres, g, part,
+               act_rt, act_p);
     // dz for pass 2: float32 dres holds dz exactly; bf16 dres is rounded, so
     // there dz is recomputed from dy and x (and res).
     const bool fp32 = sizeof(T) == 4;
@@ -628,36 +636,44 @@ static void launch_bwd_act(const BnGeom &g, hipStream_t st, bool has_res, const 
     if (ACT == kActNone && !has_res) {
         launch("bn_bwd_dx_kernel", main, bn_bwd_dx_kernel<T, V, ACT, false, 0>, grid, blk, 0, st, (const T *)dy,
                (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr, cp, n_total,
-               (T *)dw, (T *)db, (T *)dx, g);
+               (T *)dw, (T *)db, (T *)dx, g, act_rt, act_p);
     } else if (has_res && (fp32 || ACT == kActNone)) {
         launch("bn_bwd_dx_kernel", main, bn_bwd_dx_kernel<T, V, ACT, true, 1>, grid, blk, 0, st, (const T *)dy,
                (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr, cp, n_total,
-               (T *)dw, (T *)db, (T *)dx, g);
+               (T *)dw, (T *)db, (T *)dx, g, act_rt, act_p);
     } else if (has_res) {
         launch("bn_bwd_dx_kernel", main, bn_bwd_dx_kernel<T, V, ACT, true, 2>, grid, blk, 0, st, (const T *)dy,
                (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr, cp, n_total,
-               (T *)dw, (T *)db, (T *)dx, g);
+               (T *)dw, (T *)db, (T *)dx, g, act_rt, act_p);
     } else {
         launch("bn_bwd_dx_kernel", main, bn_bwd_dx_kernel<T, V, ACT, false, 2>, grid, blk, 0, st, (const T *)dy,
                (const T *)x, (const T *)res, (const T *)dres, (const T *)w, (const T *)b, sm, sr, cp, n_total,
-               (T *)dw, (T *)db, (T *)dx, g);
+               (T *)dw, (T *)db, (T *)dx, g, act_rt, act_p);
     }
 }
 
 template <typename T, int V>
-static norm_status launch_bwd(const BnGeom &g, hipStream_t st, norm_act act, const void *dy, const void *x,
-                              const void *res, const void *w, const void *b, const float *sm, const float *sr,
-                              void *dx, void *dres, void *dw, void *db, void *ws) {
+static norm_status launch_bwd(const BnGeom &g, hipStream_t st, norm_act act, float act_p, const void *dy,
+                              const void *x, const void *res, const void *w, const void *b, const float *sm,
+                              const float *sr, void *dx, void *dres, void *dw, void *db, void *ws) {
     const bool r = res != nullptr;
+    const int a = (int)act;
     switch (act) {
-    case NORM_ACT_NONE: launch_bwd_act<T, V, kActNone>(g, st, r, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws); break;
-    case NORM_ACT_RELU: launch_bwd_act<T, V, kActRelu>(g, st, r, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws); break;
-    case NORM_ACT_GELU: launch_bwd_act<T, V, kActGelu>(g, st, r, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws); break;
+    case NORM_ACT_NONE: launch_bwd_act<T, V, kActNone>(g, st, r, a, act_p, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws); break;
+    case NORM_ACT_RELU: launch_bwd_act<T, V, kActRelu>(g, st, r, a, act_p, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws); break;
+    case NORM_ACT_GELU: launch_bwd_act<T, V, kActGelu>(g, st, r, a, act_p, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws); break;
+    default: launch_bwd_act<T, V, kActGeneric>(g, st, r, a, act_p, dy, x, res, w, b, sm, sr, dx, dres, dw, db, ws); break;
     }
     return launch_status();
 }
 
-static bool act_ok(norm_act a) { return a == NORM_ACT_NONE || a == NORM_ACT_RELU || a == NORM_ACT_GELU; }
+static bool act_ok(norm_act a) { return (int)a >= 0 && (int)a < kActCount; }
+
+// The activation parameter must be finite; CELU divides by it.
+static bool act_param_ok(norm_act a, float p) {
+    if (!(p == p) || p == __builtin_inff() || p == -__builtin_inff()) return false;
+    return !(a == NORM_ACT_CELU && p == 0.0f);
+}
 
 }  // namespace mi355norm
 
@@ -669,7 +685,7 @@ extern "C" size_t bn_workspace_bytes(norm_dtype dt, int64_t Nb, int64_t C, int64
 }
 
 extern "C" norm_status bn_fwd_train(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, float eps, float momentum,
-                                    norm_act act, const void *x, const void *res, const void *w, const void *b,
+                                    norm_act act, float act_param, const void *x, const void *res, const void *w, const void *b,
                                     float *running_mean, float *running_var, float *save_mean, float *save_rstd,
                                     void *y, void *ws, size_t ws_bytes, void *stream) {
     CallScope scope;
@@ -677,6 +693,7 @@ extern "C" norm_status bn_fwd_train(norm_dtype dt, int64_t Nb, int64_t C, int64_
     if (s != NORM_OK) return s;
     if (!act_ok(act)) return NORM_ERR_ACT;
     if (!(eps >= 0.0f) || !(momentum >= 0.0f && momentum <= 1.0f)) return NORM_ERR_ARG;
+    if (!act_param_ok(act, act_param)) return NORM_ERR_ARG;
     if (C == 0) return NORM_OK;
     if (Nb * HW < 2) return NORM_ERR_ARG;  // the unbiased running variance needs n >= 2
     if (!x || !y || !save_mean || !save_rstd) return NORM_ERR_NULL;
@@ -685,33 +702,34 @@ extern "C" norm_status bn_fwd_train(norm_dtype dt, int64_t Nb, int64_t C, int64_
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool vec = bn_vec_ok(dt, HW, {x, res, y});
     if (dt == NORM_F32)
-        return vec ? launch_fwd_train<float, 4>(g, st, act, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws)
-                   : launch_fwd_train<float, 1>(g, st, act, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws);
-    return vec ? launch_fwd_train<bf16_t, 8>(g, st, act, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws)
-               : launch_fwd_train<bf16_t, 1>(g, st, act, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws);
+        return vec ? launch_fwd_train<float, 4>(g, st, act, act_param, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws)
+                   : launch_fwd_train<float, 1>(g, st, act, act_param, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws);
+    return vec ? launch_fwd_train<bf16_t, 8>(g, st, act, act_param, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws)
+               : launch_fwd_train<bf16_t, 1>(g, st, act, act_param, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws);
 }
 
 extern "C" norm_status bn_fwd_eval(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, float eps, norm_act act,
-                                   const void *x, const void *res, const void *w, const void *b,
+                                   float act_param, const void *x, const void *res, const void *w, const void *b,
                                    const float *running_mean, const float *running_var, void *y, void *stream) {
     CallScope scope;
     norm_status s = check_bn(dt, Nb, C, HW);
     if (s != NORM_OK) return s;
     if (!act_ok(act)) return NORM_ERR_ACT;
-    if (!(eps >= 0.0f)) return NORM_ERR_ARG;
+    if (!(eps >= 0.0f) || !act_param_ok(act, act_param)) return NORM_ERR_ARG;
     if (C == 0 || Nb * HW == 0) return NORM_OK;
     if (!x || !y || !running_mean || !running_var) return NORM_ERR_NULL;
     const BnGeom g = make_geom(dt, Nb, C, HW);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool vec = bn_vec_ok(dt, HW, {x, res, y});
     if (dt == NORM_F32)
-        return vec ? launch_fwd_eval<float, 4>(g, st, act, eps, x, res, w, b, running_mean, running_var, y)
-                   : launch_fwd_eval<float, 1>(g, st, act, eps, x, res, w, b, running_mean, running_var, y);
-    return vec ? launch_fwd_eval<bf16_t, 8>(g, st, act, eps, x, res, w, b, running_mean, running_var, y)
-               : launch_fwd_eval<bf16_t, 1>(g, st, act, eps, x, res, w, b, running_mean, running_var, y);
+        return vec ? launch_fwd_eval<float, 4>(g, st, act, act_param, eps, x, res, w, b, running_mean, running_var, y)
+                   : launch_fwd_eval<float, 1>(g, st, act, act_param, eps, x, res, w, b, running_mean, running_var, y);
+    return vec ? launch_fwd_eval<bf16_t, 8>(g, st, act, act_param, eps, x, res, w, b, running_mean, running_var, y)
+               : launch_fwd_eval<bf16_t, 1>(g, st, act, act_param, eps, x, res, w, b, running_mean, running_var, y);
 }
 
-extern "C" norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, norm_act act, const void *dy,
+extern "C" norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, norm_act act, float act_param,
+                              const void *dy,
                               const void *x, const void *res, const void *w, const void *b, const float *save_mean,
                               const float *save_rstd, void *dx, void *dres, void *dw, void *db, void *ws,
                               size_t ws_bytes, void *stream) {
@@ -719,6 +737,7 @@ extern "C" norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, 
     norm_status s = check_bn(dt, Nb, C, HW);
     if (s != NORM_OK) return s;
     if (!act_ok(act)) return NORM_ERR_ACT;
+    if (!act_param_ok(act, act_param)) return NORM_ERR_ARG;
     if (C == 0) return NORM_OK;
     if (Nb * HW < 2) return NORM_ERR_ARG;
     if (!dy || !x || !dx || !save_mean || !save_rstd) return NORM_ERR_NULL;
@@ -728,8 +747,8 @@ extern "C" norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool vec = bn_vec_ok(dt, HW, {dy, x, res, dx, dres});
     if (dt == NORM_F32)
-        return vec ? launch_bwd<float, 4>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws)
-                   : launch_bwd<float, 1>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws);
-    return vec ? launch_bwd<bf16_t, 8>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws)
-               : launch_bwd<bf16_t, 1>(g, st, act, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws);
+        return vec ? launch_bwd<float, 4>(g, st, act, act_param, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws)
+                   : launch_bwd<float, 1>(g, st, act, act_param, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws);
+    return vec ? launch_bwd<bf16_t, 8>(g, st, act, act_param, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws)
+               : launch_bwd<bf16_t, 1>(g, st, act, act_param, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws);
 }

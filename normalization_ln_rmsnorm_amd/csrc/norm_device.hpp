@@ -181,7 +181,13 @@ __device__ __forceinline__ double shfl_xor_d(double v, int mask) {
 //    The coefficients below are A&S's a1..a5 halved (they give Phi(-|z|)
 //    = erfc(u) / 2 directly).  This form serves the derivative, which needs
 //    both Phi and phi; the forward uses the cheaper gelu_fast below.
-enum Act : int { kActNone = 0, kActRelu = 1, kActGelu = 2 };
+enum Act : int {
+    kActNone = 0, kActRelu = 1, kActGelu = 2, kActSigmoid = 3, kActTanh = 4, kActSilu = 5,
+    kActMish = 6, kActLeakyRelu = 7, kActElu = 8, kActSelu = 9, kActCelu = 10,
+    kActSoftplus = 11, kActRelu6 = 12, kActHardsigmoid = 13, kActHardswish = 14,
+    kActCount = 15,
+    kActGeneric = 255  // template tag: the activation is chosen at run time
+};
 
 constexpr float kInvSqrt2 = 0.70710678118654752440f;
 constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
@@ -245,6 +251,72 @@ template <int ACT, bool FAST = false> __device__ __forceinline__ float act_grad(
         const NormalPdfCdf n = normal_pdf_cdf<FAST>(z);
         return fmaf(z * kInvSqrt2Pi, n.e, n.Phi);
     } else return 1.0f;
+}
+
+// The rest of the family ([ActPage] section 6), evaluated in float32 with
+// the accurate device exp / tanh / log1p / expm1.  These share one kernel
+// instantiation per shape class and select the function with a wave-uniform
+// switch; definitions and the derivative conventions at kinks are
+// PyTorch's.  `p` is the leaky slope, or alpha of ELU / CELU.
+constexpr float kSeluScale = 1.0507009873554804934f;
+constexpr float kSeluAlpha = 1.6732632423543772848f;
+
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
+__device__ __forceinline__ float softplus_f(float z) { return z > 20.0f ? z : log1pf(expf(z)); }
+
+__device__ inline float act_fwd_rt(int act, float p, float z) {
+    switch (act) {
+    case kActRelu: return z > 0.0f ? z : 0.0f;
+    case kActGelu: return 0.5f * z * (1.0f + erff(z * kInvSqrt2));
+    case kActSigmoid: return sigmoid_f(z);
+    case kActTanh: return tanhf(z);
+    case kActSilu: return z * sigmoid_f(z);
+    case kActMish: return z * tanhf(log1pf(expf(z)));
+    case kActLeakyRelu: return z > 0.0f ? z : p * z;
+    case kActElu: return z > 0.0f ? z : p * expm1f(z);
+    case kActSelu: return kSeluScale * (z > 0.0f ? z : kSeluAlpha * expm1f(z));
+    case kActCelu: return z > 0.0f ? z : p * expm1f(z / p);
+    case kActSoftplus: return softplus_f(z);
+    case kActRelu6: return fminf(fmaxf(z, 0.0f), 6.0f);
+    case kActHardsigmoid: return z <= -3.0f ? 0.0f : (z >= 3.0f ? 1.0f : z * (1.0f / 6.0f) + 0.5f);
+    case kActHardswish: return z <= -3.0f ? 0.0f : (z >= 3.0f ? z : z * (z + 3.0f) * (1.0f / 6.0f));
+    default: return z;
+    }
+}
+
+__device__ inline float act_grad_rt(int act, float p, float z) {
+    switch (act) {
+    case kActRelu: return z > 0.0f ? 1.0f : 0.0f;
+    case kActGelu: return act_grad<kActGelu, false>(z);
+    case kActSigmoid: { const float s = sigmoid_f(z); return s * (1.0f - s); }
+    case kActTanh: { const float t = tanhf(z); return 1.0f - t * t; }
+    case kActSilu: { const float s = sigmoid_f(z); return s * (1.0f + z * (1.0f - s)); }
+    case kActMish: {
+        const float t = tanhf(log1pf(expf(z)));
+        return t + z * sigmoid_f(z) * (1.0f - t * t);
+    }
+    case kActLeakyRelu: return z > 0.0f ? 1.0f : p;
+    case kActElu: return z > 0.0f ? 1.0f : p * expf(z);
+    case kActSelu: return kSeluScale * (z > 0.0f ? 1.0f : kSeluAlpha * expf(z));
+    case kActCelu: return z > 0.0f ? 1.0f : expf(z / p);
+    case kActSoftplus: return z > 20.0f ? 1.0f : sigmoid_f(z);
+    case kActRelu6: return (z > 0.0f && z < 6.0f) ? 1.0f : 0.0f;
+    case kActHardsigmoid: return (z > -3.0f && z < 3.0f) ? (1.0f / 6.0f) : 0.0f;
+    case kActHardswish: return z <= -3.0f ? 0.0f : (z < 3.0f ? z * (1.0f / 3.0f) + 0.5f : 1.0f);
+    default: return 1.0f;
+    }
+}
+
+// Compile-time activation, or the run-time one for ACT == kActGeneric.
+template <int ACT, bool FAST>
+__device__ __forceinline__ float act_fwd_any(float z, int act_rt, float p) {
+    if constexpr (ACT == kActGeneric) return act_fwd_rt(act_rt, p, z);
+    else return act_fwd<ACT, FAST>(z);
+}
+template <int ACT, bool FAST>
+__device__ __forceinline__ float act_grad_any(float z, int act_rt, float p) {
+    if constexpr (ACT == kActGeneric) return act_grad_rt(act_rt, p, z);
+    else return act_grad<ACT, FAST>(z);
 }
 
 }  // namespace mi355norm

@@ -19,7 +19,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmi355norm.so")
 
 NORM_F32, NORM_BF16 = 0, 1
-ACT = {"none": 0, "relu": 1, "gelu": 2}
+ACT = {"none": 0, "relu": 1, "gelu": 2, "sigmoid": 3, "tanh": 4, "silu": 5, "mish": 6,
+       "leaky_relu": 7, "elu": 8, "selu": 9, "celu": 10, "softplus": 11, "relu6": 12,
+       "hardsigmoid": 13, "hardswish": 14}
 STATUS = {0: "NORM_OK", -1: "NORM_ERR_NULL", -2: "NORM_ERR_SHAPE", -3: "NORM_ERR_DTYPE",
           -4: "NORM_ERR_ACT", -5: "NORM_ERR_ARG", -6: "NORM_ERR_WORKSPACE", -7: "NORM_ERR_HIP"}
 
@@ -37,10 +39,10 @@ SIGNATURES = {
     "rms_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64]),
     "rms_bwd": (_I, [_I, _I64, _I64, _V, _V, _V, _V, _V, _V, _V, _SZ, _V]),
     "bn_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64]),
-    "bn_fwd_train": (_I, [_I, _I64, _I64, _I64, _F, _F, _I, _V, _V, _V, _V, _V, _V, _V, _V,
+    "bn_fwd_train": (_I, [_I, _I64, _I64, _I64, _F, _F, _I, _F, _V, _V, _V, _V, _V, _V, _V, _V,
                           _V, _V, _SZ, _V]),
-    "bn_fwd_eval": (_I, [_I, _I64, _I64, _I64, _F, _I, _V, _V, _V, _V, _V, _V, _V, _V]),
-    "bn_bwd": (_I, [_I, _I64, _I64, _I64, _I, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
+    "bn_fwd_eval": (_I, [_I, _I64, _I64, _I64, _F, _I, _F, _V, _V, _V, _V, _V, _V, _V, _V]),
+    "bn_bwd": (_I, [_I, _I64, _I64, _I64, _I, _F, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
                     _SZ, _V]),
     "norm_status_str": (ctypes.c_char_p, [_I]),
     "norm_arm_kernel_events": (None, [ctypes.POINTER(ctypes.c_void_p), _I]),
@@ -225,8 +227,11 @@ def bn_workspace_bytes(dtype, Nb, C, HW):
 
 
 def bn_fwd_train(x, w=None, b=None, running_mean=None, running_var=None, eps=1e-5, momentum=0.1,
-                 act="none", res=None, *, y=None, save_mean=None, save_rstd=None, ws=None):
-    """Training forward; updates running stats in place.  Returns (y, save_mean, save_rstd)."""
+                 act="none", res=None, *, act_param=0.0, y=None, save_mean=None, save_rstd=None,
+                 ws=None):
+    """Training forward; updates running stats in place.  Returns (y, save_mean, save_rstd).
+
+    act_param: negative slope for leaky_relu, alpha for elu / celu."""
     Nb, C, HW = bn_shape(x)
     _same(res, x, "res"); _same(w, x, "w"); _same(b, x, "b")
     y = torch.empty_like(x) if y is None else y
@@ -234,24 +239,27 @@ def bn_fwd_train(x, w=None, b=None, running_mean=None, running_var=None, eps=1e-
     save_rstd = _stat(save_rstd, C, x.device, "save_rstd")
     ws, nbytes = _workspace(lib().bn_workspace_bytes(_dt(x), Nb, C, HW), x.device, ws)
     _check("bn_fwd_train", lib().bn_fwd_train(
-        _dt(x), Nb, C, HW, float(eps), float(momentum), ACT[act], _ptr(x), _ptr(res), _ptr(w),
+        _dt(x), Nb, C, HW, float(eps), float(momentum), ACT[act], float(act_param), _ptr(x),
+        _ptr(res), _ptr(w),
         _ptr(b), _ptr(running_mean), _ptr(running_var), _ptr(save_mean), _ptr(save_rstd), _ptr(y),
         _ptr(ws), nbytes, _stream(x.device)))
     return y, save_mean, save_rstd
 
 
-def bn_fwd_eval(x, w, b, running_mean, running_var, eps=1e-5, act="none", res=None, *, y=None):
+def bn_fwd_eval(x, w, b, running_mean, running_var, eps=1e-5, act="none", res=None, *,
+                act_param=0.0, y=None):
     Nb, C, HW = bn_shape(x)
     _same(res, x, "res"); _same(w, x, "w"); _same(b, x, "b")
     y = torch.empty_like(x) if y is None else y
     _check("bn_fwd_eval", lib().bn_fwd_eval(
-        _dt(x), Nb, C, HW, float(eps), ACT[act], _ptr(x), _ptr(res), _ptr(w), _ptr(b),
+        _dt(x), Nb, C, HW, float(eps), ACT[act], float(act_param), _ptr(x), _ptr(res), _ptr(w),
+        _ptr(b),
         _ptr(running_mean), _ptr(running_var), _ptr(y), _stream(x.device)))
     return y
 
 
-def bn_bwd(dy, x, w, b, save_mean, save_rstd, act="none", res=None, *, want_dw=True,
-           want_db=True, dx=None, dres=None, dw=None, db=None, ws=None):
+def bn_bwd(dy, x, w, b, save_mean, save_rstd, act="none", res=None, *, act_param=0.0,
+           want_dw=True, want_db=True, dx=None, dres=None, dw=None, db=None, ws=None):
     """Returns (dx, dres, dw, db); dres is None without a residual."""
     Nb, C, HW = bn_shape(x)
     _same(dy, x, "dy"); _same(res, x, "res"); _same(w, x, "w"); _same(b, x, "b")
@@ -264,7 +272,8 @@ def bn_bwd(dy, x, w, b, save_mean, save_rstd, act="none", res=None, *, want_dw=T
         db = torch.empty(C, dtype=x.dtype, device=x.device)
     ws, nbytes = _workspace(lib().bn_workspace_bytes(_dt(x), Nb, C, HW), x.device, ws)
     _check("bn_bwd", lib().bn_bwd(
-        _dt(x), Nb, C, HW, ACT[act], _ptr(dy), _ptr(x), _ptr(res), _ptr(w), _ptr(b),
+        _dt(x), Nb, C, HW, ACT[act], float(act_param), _ptr(dy), _ptr(x), _ptr(res), _ptr(w),
+        _ptr(b),
         _ptr(save_mean), _ptr(save_rstd), _ptr(dx), _ptr(dres), _ptr(dw), _ptr(db), _ptr(ws),
         nbytes, _stream(x.device)))
     return dx, dres, dw, db

@@ -19,7 +19,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libnorm_oracle.so")
 _lib = None
 
-ACT = {"none": 0, "relu": 1, "gelu": 2}
+ACT = {"none": 0, "relu": 1, "gelu": 2, "sigmoid": 3, "tanh": 4, "silu": 5, "mish": 6,
+       "leaky_relu": 7, "elu": 8, "selu": 9, "celu": 10, "softplus": 11, "relu6": 12,
+       "hardsigmoid": 13, "hardswish": 14}
 
 _D = ctypes.POINTER(ctypes.c_double)
 _I64 = ctypes.c_int64
@@ -34,17 +36,17 @@ def _load():
         _b.build()
     lib = ctypes.CDLL(_LIB_PATH)
     sigs = {
-        "orc_act_vec": [ctypes.c_int, ctypes.c_int, _I64, _D, _D],
+        "orc_act_vec": [ctypes.c_int, ctypes.c_double, ctypes.c_int, _I64, _D, _D],
         "orc_ln_fwd": [_I64, _I64, ctypes.c_double, _D, _D, _D, _D, _D, _D],
         "orc_ln_bwd": [_I64, _I64, ctypes.c_double, _D, _D, _D, _D, _D, _D],
         "orc_rms_fwd": [_I64, _I64, ctypes.c_double, _D, _D, _D, _D],
         "orc_rms_bwd": [_I64, _I64, ctypes.c_double, _D, _D, _D, _D, _D],
         "orc_bn_stats": [_I64, _I64, _I64, _D, _D, _D],
         "orc_bn_fwd_train": [_I64, _I64, _I64, ctypes.c_double, ctypes.c_double,
-                             ctypes.c_int, _D, _D, _D, _D, _D, _D, _D, _D, _D],
-        "orc_bn_fwd_eval": [_I64, _I64, _I64, ctypes.c_double, ctypes.c_int,
+                             ctypes.c_int, ctypes.c_double, _D, _D, _D, _D, _D, _D, _D, _D, _D],
+        "orc_bn_fwd_eval": [_I64, _I64, _I64, ctypes.c_double, ctypes.c_int, ctypes.c_double,
                             _D, _D, _D, _D, _D, _D, _D],
-        "orc_bn_bwd": [_I64, _I64, _I64, ctypes.c_double, ctypes.c_int,
+        "orc_bn_bwd": [_I64, _I64, _I64, ctypes.c_double, ctypes.c_int, ctypes.c_double,
                        _D, _D, _D, _D, _D, _D, _D, _D, _D],
         "orc_welford": [_I64, _D, _D],
         "orc_chan_merge": [_D, _D, _D],
@@ -90,10 +92,12 @@ def _f(a, bf16):
     return widen(a, bf16) if a is not None else None
 
 
-def act(name, z, grad=False):
+def act(name, z, grad=False, param=0.0):
+    """act(z), or act'(z) with grad=True; `param` is the leaky slope or the
+    elu / celu alpha."""
     z = widen(z)
     out = np.empty_like(z)
-    _load().orc_act_vec(ACT[name], int(bool(grad)), z.size, _p(z), _p(out))
+    _load().orc_act_vec(ACT[name], float(param), int(bool(grad)), z.size, _p(z), _p(out))
     return out
 
 
@@ -146,7 +150,7 @@ def bn_stats(x, bf16=False):
 
 
 def bn_fwd_train(x, res=None, w=None, b=None, running_mean=None, running_var=None,
-                 eps=1e-5, momentum=0.1, act="none", bf16=False):
+                 eps=1e-5, momentum=0.1, act="none", bf16=False, act_param=0.0):
     """Returns (y, save_mean, save_rstd, new_running_mean, new_running_var).
 
     The running statistics are float32 on the GPU side; pass them as they
@@ -156,23 +160,23 @@ def bn_fwd_train(x, res=None, w=None, b=None, running_mean=None, running_var=Non
     rv = widen(running_var).copy() if running_var is not None else None
     Nb, C, HW = x.shape
     y = np.empty_like(x); sm = np.empty(C); sr = np.empty(C)
-    _load().orc_bn_fwd_train(Nb, C, HW, eps, momentum, ACT[act], _p(x), _p(res),
+    _load().orc_bn_fwd_train(Nb, C, HW, eps, momentum, ACT[act], float(act_param), _p(x), _p(res),
                              _p(w), _p(b), _p(rm), _p(rv), _p(y), _p(sm), _p(sr))
     return y, sm, sr, rm, rv
 
 
 def bn_fwd_eval(x, running_mean, running_var, res=None, w=None, b=None, eps=1e-5,
-                act="none", bf16=False):
+                act="none", bf16=False, act_param=0.0):
     x = _f(x, bf16); res = _f(res, bf16); w = _f(w, bf16); b = _f(b, bf16)
     rm = widen(running_mean); rv = widen(running_var)
     Nb, C, HW = x.shape
     y = np.empty_like(x)
-    _load().orc_bn_fwd_eval(Nb, C, HW, eps, ACT[act], _p(x), _p(res), _p(w), _p(b),
+    _load().orc_bn_fwd_eval(Nb, C, HW, eps, ACT[act], float(act_param), _p(x), _p(res), _p(w), _p(b),
                             _p(rm), _p(rv), _p(y))
     return y
 
 
-def bn_bwd(dy, x, res=None, w=None, b=None, eps=1e-5, act="none", bf16=False):
+def bn_bwd(dy, x, res=None, w=None, b=None, eps=1e-5, act="none", bf16=False, act_param=0.0):
     """Returns (dx, dres, dw, db); dres is None when there is no residual."""
     dy = _f(dy, bf16); x = _f(x, bf16); res = _f(res, bf16)
     w = _f(w, bf16); b = _f(b, bf16)
@@ -180,7 +184,7 @@ def bn_bwd(dy, x, res=None, w=None, b=None, eps=1e-5, act="none", bf16=False):
     dx = np.empty_like(x)
     dres = np.empty_like(x) if res is not None else None
     dw = np.empty(C); db = np.empty(C)
-    _load().orc_bn_bwd(Nb, C, HW, eps, ACT[act], _p(dy), _p(x), _p(res), _p(w), _p(b),
+    _load().orc_bn_bwd(Nb, C, HW, eps, ACT[act], float(act_param), _p(dy), _p(x), _p(res), _p(w), _p(b),
                        _p(dx), _p(dres), _p(dw), _p(db))
     return dx, dres, dw, db
 

@@ -25,21 +25,56 @@ int orc_num_threads(void) {
 #endif
 }
 
-/* ReLU and the exact (error-function) GELU, with their derivatives.
- * [ActPage] section 5: the backward multiplies the incoming gradient by the
- * analytic derivative evaluated at the saved pre-activation input; ReLU's
- * derivative is 0 where the input is <= 0 and 1 elsewhere; GELU uses the
- * error-function form.  GELU(z) = z * Phi(z), Phi the standard normal CDF,
- * so GELU'(z) = Phi(z) + z * phi(z) with phi the standard normal density. */
-double orc_act(int act, double z) {
+/* Activations and their derivatives.  [ActPage] section 5: the backward
+ * multiplies the incoming gradient by the analytic derivative evaluated at
+ * the saved pre-activation input; ReLU's derivative is 0 where the input is
+ * <= 0 and 1 elsewhere; GELU uses the error-function form.  Section 6 lists
+ * the activation family (sigmoid, GELU, SiLU, Mish, LeakyReLU, ELU, CELU,
+ * ... with parameters such as a leaky slope or an ELU alpha).  The
+ * definitions and the conventions at kinks are PyTorch's (the pages' layers
+ * are PyTorch drop-ins):
+ *   relu      max(z, 0);                      ' = [z > 0]
+ *   gelu      z Phi(z);                       ' = Phi(z) + z phi(z)
+ *   sigmoid   s = 1 / (1 + e^-z);             ' = s (1 - s)
+ *   tanh      t = tanh z;                     ' = 1 - t^2
+ *   silu      z s;                            ' = s (1 + z (1 - s))
+ *   softplus  log(1 + e^z) (z if z > 20);     ' = s (1 if z > 20)
+ *   mish      z tanh(log(1 + e^z));           ' = T + z s (1 - T^2), T = tanh(log(1+e^z))
+ *   leaky     z if z > 0 else p z;            ' = 1 if z > 0 else p
+ *   elu       z if z > 0 else p (e^z - 1);    ' = 1 if z > 0 else p e^z
+ *   selu      S (z if z > 0 else A (e^z - 1)); ' = S (1 if z > 0 else A e^z)
+ *   celu      z if z > 0 else p (e^(z/p) - 1); ' = 1 if z > 0 else e^(z/p)
+ *   relu6     min(max(z, 0), 6);              ' = [0 < z < 6]
+ *   hardsigmoid min(max(z + 3, 0), 6) / 6;    ' = 1/6 on (-3, 3), else 0
+ *   hardswish z min(max(z + 3, 0), 6) / 6;    ' = 0 (z <= -3), z/3 + 1/2 (z < 3), 1
+ * with S = 1.0507009873554804934, A = 1.6732632423543772848 (the SELU
+ * constants). */
+static const double kSeluScale = 1.0507009873554804934193349852946;
+static const double kSeluAlpha = 1.6732632423543772848170429916717;
+
+static double sigm(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+double orc_act(int act, double p, double z) {
     switch (act) {
     case ORC_ACT_RELU: return z > 0.0 ? z : 0.0;
     case ORC_ACT_GELU: return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));
+    case ORC_ACT_SIGMOID: return sigm(z);
+    case ORC_ACT_TANH: return tanh(z);
+    case ORC_ACT_SILU: return z * sigm(z);
+    case ORC_ACT_SOFTPLUS: return z > 20.0 ? z : log1p(exp(z));
+    case ORC_ACT_MISH: return z * tanh(log1p(exp(z)));
+    case ORC_ACT_LEAKY_RELU: return z > 0.0 ? z : p * z;
+    case ORC_ACT_ELU: return z > 0.0 ? z : p * expm1(z);
+    case ORC_ACT_SELU: return kSeluScale * (z > 0.0 ? z : kSeluAlpha * expm1(z));
+    case ORC_ACT_CELU: return z > 0.0 ? z : p * expm1(z / p);
+    case ORC_ACT_RELU6: return z < 0.0 ? 0.0 : (z > 6.0 ? 6.0 : z);
+    case ORC_ACT_HARDSIGMOID: return z <= -3.0 ? 0.0 : (z >= 3.0 ? 1.0 : z / 6.0 + 0.5);
+    case ORC_ACT_HARDSWISH: return z <= -3.0 ? 0.0 : (z >= 3.0 ? z : z * (z + 3.0) / 6.0);
     default: return z;
     }
 }
 
-double orc_act_grad(int act, double z) {
+double orc_act_grad(int act, double p, double z) {
     switch (act) {
     case ORC_ACT_RELU: return z > 0.0 ? 1.0 : 0.0;
     case ORC_ACT_GELU: {
@@ -47,13 +82,28 @@ double orc_act_grad(int act, double z) {
         double phi = exp(-0.5 * z * z) / sqrt(2.0 * M_PI);
         return Phi + z * phi;
     }
+    case ORC_ACT_SIGMOID: { double s = sigm(z); return s * (1.0 - s); }
+    case ORC_ACT_TANH: { double t = tanh(z); return 1.0 - t * t; }
+    case ORC_ACT_SILU: { double s = sigm(z); return s * (1.0 + z * (1.0 - s)); }
+    case ORC_ACT_SOFTPLUS: return z > 20.0 ? 1.0 : sigm(z);
+    case ORC_ACT_MISH: {
+        double t = tanh(log1p(exp(z)));
+        return t + z * sigm(z) * (1.0 - t * t);
+    }
+    case ORC_ACT_LEAKY_RELU: return z > 0.0 ? 1.0 : p;
+    case ORC_ACT_ELU: return z > 0.0 ? 1.0 : p * exp(z);
+    case ORC_ACT_SELU: return kSeluScale * (z > 0.0 ? 1.0 : kSeluAlpha * exp(z));
+    case ORC_ACT_CELU: return z > 0.0 ? 1.0 : exp(z / p);
+    case ORC_ACT_RELU6: return (z > 0.0 && z < 6.0) ? 1.0 : 0.0;
+    case ORC_ACT_HARDSIGMOID: return (z > -3.0 && z < 3.0) ? 1.0 / 6.0 : 0.0;
+    case ORC_ACT_HARDSWISH: return z <= -3.0 ? 0.0 : (z < 3.0 ? z / 3.0 + 0.5 : 1.0);
     default: return 1.0;
     }
 }
 
-void orc_act_vec(int act, int grad, int64_t n, const double *z, double *out) {
+void orc_act_vec(int act, double p, int grad, int64_t n, const double *z, double *out) {
     for (int64_t i = 0; i < n; ++i)
-        out[i] = grad ? orc_act_grad(act, z[i]) : orc_act(act, z[i]);
+        out[i] = grad ? orc_act_grad(act, p, z[i]) : orc_act(act, p, z[i]);
 }
 
 /* ---------------------------------------------------------------- LayerNorm
@@ -245,7 +295,7 @@ void orc_bn_stats(int64_t Nb, int64_t C, int64_t HW, const double *x,
  * where the variance fed to the running estimate is the unbiased one
  * (var * n / (n - 1)), as PyTorch does. */
 void orc_bn_fwd_train(int64_t Nb, int64_t C, int64_t HW, double eps,
-                      double momentum, int act, const double *x,
+                      double momentum, int act, double act_p, const double *x,
                       const double *res, const double *w, const double *b,
                       double *running_mean, double *running_var, double *y,
                       double *save_mean, double *save_rstd) {
@@ -262,7 +312,7 @@ void orc_bn_fwd_train(int64_t Nb, int64_t C, int64_t HW, double eps,
                 int64_t idx = (bi * C + c) * HW + k;
                 double z = (x[idx] - mu[c]) * r * wc + bc;
                 if (res) z += res[idx];
-                y[idx] = orc_act(act, z);
+                y[idx] = orc_act(act, act_p, z);
             }
         if (save_mean) save_mean[c] = mu[c];
         if (save_rstd) save_rstd[c] = r;
@@ -279,7 +329,7 @@ void orc_bn_fwd_train(int64_t Nb, int64_t C, int64_t HW, double eps,
 /* Eval forward: [NormPage] "BatchNorm" section -- inference reads the
  * running statistics in place of the batch statistics. */
 void orc_bn_fwd_eval(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
-                     const double *x, const double *res, const double *w,
+                     double act_p, const double *x, const double *res, const double *w,
                      const double *b, const double *running_mean,
                      const double *running_var, double *y) {
 #pragma omp parallel for schedule(dynamic, 1)
@@ -291,7 +341,7 @@ void orc_bn_fwd_eval(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
                 int64_t idx = (bi * C + c) * HW + k;
                 double z = (x[idx] - running_mean[c]) * r * wc + bc;
                 if (res) z += res[idx];
-                y[idx] = orc_act(act, z);
+                y[idx] = orc_act(act, act_p, z);
             }
     }
 }
@@ -304,7 +354,7 @@ void orc_bn_fwd_eval(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
  *   db   = sum dz,   dw = sum dz * xhat
  *   dx   = (w * rstd / n) * (n * dz - db - xhat * dw).                    */
 void orc_bn_bwd(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
-                const double *dy, const double *x, const double *res,
+                double act_p, const double *dy, const double *x, const double *res,
                 const double *w, const double *b, double *dx, double *dres,
                 double *dw, double *db) {
     double *mu = (double *)malloc(sizeof(double) * (C > 0 ? C : 1));
@@ -321,7 +371,7 @@ void orc_bn_bwd(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
                 int64_t idx = (bi * C + c) * HW + k;
                 double xhat = (x[idx] - mu[c]) * r;
                 double z = xhat * wc + bc + (res ? res[idx] : 0.0);
-                double dz = dy[idx] * orc_act_grad(act, z);
+                double dz = dy[idx] * orc_act_grad(act, act_p, z);
                 if (dres) dres[idx] = dz;
                 sum_dz += dz;
                 sum_dz_xhat += dz * xhat;
@@ -331,7 +381,7 @@ void orc_bn_bwd(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
                 int64_t idx = (bi * C + c) * HW + k;
                 double xhat = (x[idx] - mu[c]) * r;
                 double z = xhat * wc + bc + (res ? res[idx] : 0.0);
-                double dz = dy[idx] * orc_act_grad(act, z);
+                double dz = dy[idx] * orc_act_grad(act, act_p, z);
                 dx[idx] = (wc * r / n) * (n * dz - sum_dz - xhat * sum_dz_xhat);
             }
         if (db) db[c] = sum_dz;

@@ -32,13 +32,20 @@
 extern "C" {
 #endif
 
-enum { ORC_ACT_NONE = 0, ORC_ACT_RELU = 1, ORC_ACT_GELU = 2 };
+enum {
+    ORC_ACT_NONE = 0, ORC_ACT_RELU = 1, ORC_ACT_GELU = 2, ORC_ACT_SIGMOID = 3,
+    ORC_ACT_TANH = 4, ORC_ACT_SILU = 5, ORC_ACT_MISH = 6, ORC_ACT_LEAKY_RELU = 7,
+    ORC_ACT_ELU = 8, ORC_ACT_SELU = 9, ORC_ACT_CELU = 10, ORC_ACT_SOFTPLUS = 11,
+    ORC_ACT_RELU6 = 12, ORC_ACT_HARDSIGMOID = 13, ORC_ACT_HARDSWISH = 14
+};
 
-/* Activations and their derivatives ([ActPage] sections 5 and 6). */
-double orc_act(int act, double z);
-double orc_act_grad(int act, double z);
+/* Activations and their derivatives ([ActPage] sections 5 and 6).  `p` is
+ * the activation's parameter: the negative slope of leaky_relu, alpha of
+ * elu and celu; ignored otherwise. */
+double orc_act(int act, double p, double z);
+double orc_act_grad(int act, double p, double z);
 /* Element-wise over an array: out = act(z), or act'(z) when grad != 0. */
-void orc_act_vec(int act, int grad, int64_t n, const double *z, double *out);
+void orc_act_vec(int act, double p, int grad, int64_t n, const double *z, double *out);
 
 /* LayerNorm ([NormPage] "LayerNorm" section). */
 void orc_ln_fwd(int64_t M, int64_t N, double eps, const double *x,
@@ -58,16 +65,16 @@ void orc_rms_bwd(int64_t M, int64_t N, double eps, const double *dy,
 void orc_bn_stats(int64_t Nb, int64_t C, int64_t HW, const double *x,
                   double *mean, double *var_biased);
 void orc_bn_fwd_train(int64_t Nb, int64_t C, int64_t HW, double eps,
-                      double momentum, int act, const double *x,
+                      double momentum, int act, double act_p, const double *x,
                       const double *res, const double *w, const double *b,
                       double *running_mean, double *running_var, double *y,
                       double *save_mean, double *save_rstd);
 void orc_bn_fwd_eval(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
-                     const double *x, const double *res, const double *w,
+                     double act_p, const double *x, const double *res, const double *w,
                      const double *b, const double *running_mean,
                      const double *running_var, double *y);
 void orc_bn_bwd(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
-                const double *dy, const double *x, const double *res,
+                double act_p, const double *dy, const double *x, const double *res,
                 const double *w, const double *b, double *dx, double *dres,
                 double *dw, double *db);
 

@@ -92,28 +92,47 @@ def round_bf16_f32(a):
     return f32_to_bf16_bits(a)
 
 
-def avoid_relu_kink(orc, inp, dtype, eps, delta=1e-3, step=None):
-    """Move the residual (or x) so no pre-activation lies within `delta` of 0.
+# Pre-activation values where an activation's derivative jumps (PyTorch's
+# definitions; CELU and the smooth ones have none, softplus's switch to the
+# identity at 20 moves values by about 2e-9 only).
+KINKS = {"relu": (0.0,), "leaky_relu": (0.0,), "elu": (0.0,), "selu": (0.0,),
+         "relu6": (0.0, 6.0), "hardsigmoid": (-3.0, 3.0), "hardswish": (-3.0, 3.0)}
 
-    ReLU's derivative jumps at z = 0, so an element whose z is within
-    rounding distance of 0 has two valid gradients (the GPU's float32 z and
-    the oracle's float64 z may fall on different sides).  The test inputs are
-    shifted away from the kink, using the oracle's z, so the mask is unique.
-    Returns the edited copy of `inp` and the number of elements moved."""
+
+def avoid_kinks(orc, inp, dtype, eps, act, delta=1e-3, step=None):
+    """Move the residual (or x) so no pre-activation lies within `delta` of a
+    kink of `act`.
+
+    Where the derivative jumps, an element whose z is within rounding
+    distance of the kink has two valid gradients (the GPU's float32 z and the
+    oracle's float64 z may fall on different sides).  The test inputs are
+    shifted away from every kink, using the oracle's z, so the choice is
+    unique.  Returns the edited copy of `inp` and the number of elements
+    moved."""
+    kinks = np.asarray(KINKS.get(act, ()), dtype=np.float64)
     out = dict(inp)
+    if kinks.size == 0:
+        return out, 0
     bf16 = dtype == "bf16"
     step = step if step is not None else (0.0625 if bf16 else 4 * delta)
     moved = 0
-    for _ in range(4):
+    for _ in range(6):
         y, _, _, _, _ = orc.bn_fwd_train(out["x"], out["res"], out["w"], out["b"], eps=eps,
                                          act="none", bf16=bf16)
-        near = np.abs(y) < delta
+        d = y[..., None] - kinks
+        j = np.abs(d).argmin(axis=-1)
+        nearest = np.take_along_axis(d, j[..., None], axis=-1)[..., 0]
+        near = np.abs(nearest) < delta
         if not near.any():
             return out, moved
         moved += int(near.sum())
-        shift = np.where(y >= 0, step, -step)
+        shift = np.where(nearest >= 0, step, -step)
         key = "res" if out["res"] is not None else "x"
         base = orc.widen(out[key], bf16=bf16)
         edited = (base + np.where(near, shift, 0.0)).astype(np.float32)
         out[key] = round_bf16_f32(edited) if bf16 else edited
-    raise AssertionError("could not move the pre-activations away from the ReLU kink")
+    raise AssertionError(f"could not move the pre-activations away from the {act} kinks")
+
+
+def avoid_relu_kink(orc, inp, dtype, eps, delta=1e-3, step=None):
+    return avoid_kinks(orc, inp, dtype, eps, "relu", delta, step)

@@ -89,19 +89,22 @@ def test_row_errors(lib):
 def test_bn_errors(lib):
     ws = lib.bn_workspace_bytes(F32, 2, 3, 5)
     assert ws > 0
-    args = lambda **k: dict(dict(dt=F32, Nb=2, C=3, HW=5, eps=1e-5, mom=0.1, act=0, x=P, res=NULL,
+    args = lambda **k: dict(dict(dt=F32, Nb=2, C=3, HW=5, eps=1e-5, mom=0.1, act=0, ap=0.0, x=P, res=NULL,
                                  w=NULL, b=NULL, rm=NULL, rv=NULL, sm=P, sr=P, y=P, ws=P,
                                  wsb=ws, s=NULL), **k)
 
     def train(**k):
         a = args(**k)
         return lib.bn_fwd_train(a["dt"], a["Nb"], a["C"], a["HW"], a["eps"], a["mom"], a["act"],
-                                a["x"], a["res"], a["w"], a["b"], a["rm"], a["rv"], a["sm"],
-                                a["sr"], a["y"], a["ws"], a["wsb"], a["s"])
+                                a["ap"], a["x"], a["res"], a["w"], a["b"], a["rm"], a["rv"],
+                                a["sm"], a["sr"], a["y"], a["ws"], a["wsb"], a["s"])
 
     assert train(dt=4) == EDTYPE
-    assert train(act=3) == EACT
+    assert train(act=15) == EACT
     assert train(act=-1) == EACT
+    assert train(act=10, ap=0.0) == EARG    # CELU divides by its alpha
+    assert train(act=7, ap=float("nan")) == EARG
+    assert train(act=8, ap=float("inf")) == EARG
     assert train(mom=1.5) == EARG
     assert train(mom=-0.1) == EARG
     assert train(eps=-1.0) == EARG
@@ -113,18 +116,22 @@ def test_bn_errors(lib):
     assert train(ws=NULL) == EWS
     assert train(wsb=ws - 1) == EWS
     assert train(C=0) == OK
-    assert lib.bn_fwd_eval(F32, 2, 3, 5, 1e-5, 0, P, NULL, NULL, NULL, NULL, P, P, NULL) == ENULL
-    assert lib.bn_fwd_eval(F32, 2, 3, 5, 1e-5, 5, P, NULL, NULL, NULL, P, P, P, NULL) == EACT
-    assert lib.bn_fwd_eval(F32, 0, 3, 5, 1e-5, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == OK
+    assert lib.bn_fwd_eval(F32, 2, 3, 5, 1e-5, 0, 0.0, P, NULL, NULL, NULL, NULL, P, P, NULL) == ENULL
+    assert lib.bn_fwd_eval(F32, 2, 3, 5, 1e-5, 25, 0.0, P, NULL, NULL, NULL, P, P, P, NULL) == EACT
+    assert lib.bn_fwd_eval(F32, 2, 3, 5, 1e-5, 10, 0.0, P, NULL, NULL, NULL, P, P, P, NULL) == EARG
+    assert lib.bn_fwd_eval(F32, 0, 3, 5, 1e-5, 0, 0.0, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+                           NULL) == OK
     # backward: residual without dres, missing saved statistics, workspace
-    assert lib.bn_bwd(F32, 2, 3, 5, 0, P, P, P, NULL, NULL, P, P, P, NULL, NULL, NULL, P, ws,
+    assert lib.bn_bwd(F32, 2, 3, 5, 0, 0.0, P, P, P, NULL, NULL, P, P, P, NULL, NULL, NULL, P, ws,
                       NULL) == ENULL
-    assert lib.bn_bwd(F32, 2, 3, 5, 0, P, P, NULL, NULL, NULL, NULL, P, P, NULL, NULL, NULL, P, ws,
-                      NULL) == ENULL
-    assert lib.bn_bwd(F32, 2, 3, 5, 0, P, P, NULL, NULL, NULL, P, P, P, NULL, NULL, NULL, P, 8,
+    assert lib.bn_bwd(F32, 2, 3, 5, 0, 0.0, P, P, NULL, NULL, NULL, NULL, P, P, NULL, NULL, NULL, P,
+                      ws, NULL) == ENULL
+    assert lib.bn_bwd(F32, 2, 3, 5, 0, 0.0, P, P, NULL, NULL, NULL, P, P, P, NULL, NULL, NULL, P, 8,
                       NULL) == EWS
-    assert lib.bn_bwd(F32, 2, 3, 5, 7, P, P, NULL, NULL, NULL, P, P, P, NULL, NULL, NULL, P, ws,
+    assert lib.bn_bwd(F32, 2, 3, 5, 17, 0.0, P, P, NULL, NULL, NULL, P, P, P, NULL, NULL, NULL, P, ws,
                       NULL) == EACT
+    assert lib.bn_bwd(F32, 2, 3, 5, 10, 0.0, P, P, NULL, NULL, NULL, P, P, P, NULL, NULL, NULL, P, ws,
+                      NULL) == EARG
     assert lib.bn_workspace_bytes(F32, -1, 3, 5) == 0
 
 

@@ -1,9 +1,9 @@
 """GPU parity: BatchNorm training forward, eval forward and backward (with
-the fused residual and ReLU / exact-GELU activation) through the C ABI
-against the float64 oracle, element by element.
+the fused residual and each fused activation) through the C ABI against the
+float64 oracle, element by element.
 
-ReLU cases move the inputs off the kink of the derivative first
-(tests._parity.avoid_relu_kink): at z = 0 either gradient is valid.
+Cases whose activation has a derivative jump move the inputs off the kinks
+first (tests._parity.avoid_kinks): at a kink either gradient is valid.
 """
 import dataclasses
 
@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests._parity import avoid_relu_kink, check, to_dev, to_f64
+from tests._parity import avoid_kinks, check, round_bf16_f32, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -24,15 +24,24 @@ def _wl(dtype, act, residual):
     return dataclasses.replace(base, act=act, residual=residual)
 
 
+def _scale_w(orc, inp, dtype, k):
+    """Multiply the affine weight by a power of two (exact in both formats)."""
+    out = dict(inp)
+    w = orc.widen(inp["w"], bf16=dtype == "bf16") * k
+    out["w"] = round_bf16_f32(w.astype(np.float32)) if dtype == "bf16" else w.astype(np.float32)
+    return out
+
+
 def run_case(orc, dtype, Nb, C, HW, act, residual, with_wb=True, eval_after=True, report=None,
-             inp=None, wl=None):
+             inp=None, wl=None, act_param=0.0, w_scale=1):
     wl = wl or _wl(dtype, act, residual)
     if inp is None:
         inp = gen_bn(wl, Nb=Nb, C=C, HW=HW)
     bf16 = dtype == "bf16"
     eps, mom = wl.eps, wl.momentum
-    if act == "relu":
-        inp, moved = avoid_relu_kink(orc, inp, dtype, eps)
+    if w_scale != 1:
+        inp = _scale_w(orc, inp, dtype, w_scale)
+    inp, moved = avoid_kinks(orc, inp, dtype, eps, act)
     shape = (Nb, C, HW)
     x = to_dev(inp["x"], dtype)
     res = to_dev(inp["res"], dtype) if residual else None
@@ -45,27 +54,31 @@ def run_case(orc, dtype, Nb, C, HW, act, residual, with_wb=True, eval_after=True
     b_np = inp["b"] if with_wb else None
     res_np = inp["res"] if residual else None
 
-    y, sm, sr = nl.bn_fwd_train(x, w, b, rm, rv, eps, mom, act, res)
-    dx, dres, dw, db = nl.bn_bwd(dy, x, w, b, sm, sr, act, res, want_dw=with_wb, want_db=with_wb)
-    ye = nl.bn_fwd_eval(x, w, b, rm, rv, eps, act, res) if eval_after else None
+    ap = act_param
+    y, sm, sr = nl.bn_fwd_train(x, w, b, rm, rv, eps, mom, act, res, act_param=ap)
+    dx, dres, dw, db = nl.bn_bwd(dy, x, w, b, sm, sr, act, res, act_param=ap, want_dw=with_wb,
+                                 want_db=with_wb)
+    ye = nl.bn_fwd_eval(x, w, b, rm, rv, eps, act, res, act_param=ap) if eval_after else None
     torch.cuda.synchronize()
 
     ry, rsm, rsr, rrm, rrv = orc.bn_fwd_train(inp["x"], res_np, w_np, b_np, inp["running_mean"],
                                               inp["running_var"], eps=eps, momentum=mom, act=act,
-                                              bf16=bf16)
+                                              bf16=bf16, act_param=ap)
     rdx, rdres, rdw, rdb = orc.bn_bwd(inp["dy"], inp["x"], res_np, w_np, b_np, eps=eps, act=act,
-                                      bf16=bf16)
-    tag = f"bn/{dtype}/{Nb}x{C}x{HW}/{act}/res={residual}"
+                                      bf16=bf16, act_param=ap)
+    tag = f"bn/{dtype}/{Nb}x{C}x{HW}/{act}({ap})/res={residual}"
     ch = (0, 2)  # bf16 floor taken per channel
     check(f"{tag} y", to_f64(y), ry, dtype, group_axis=ch, report=report)
     check(f"{tag} save_mean", to_f64(sm), rsm, "f32", report=report)
     check(f"{tag} save_rstd", to_f64(sr), rsr, "f32", report=report)
     check(f"{tag} running_mean", to_f64(rm), rrm, "f32", report=report)
     check(f"{tag} running_var", to_f64(rv), rrv, "f32", report=report)
-    # Scale of the terms dx is formed from: |w_c * rstd_c| * max |dy| per channel.
+    # Scale of the terms dx is formed from: |w_c * rstd_c| * max |dz| per
+    # channel, dz = dy * act'(z) (oracle values).
     wabs = np.abs(orc.widen(w_np, bf16=bf16)) if with_wb else np.ones(C)
-    dymax = np.abs(orc.widen(inp["dy"], bf16=bf16)).max(axis=(0, 2))
-    dx_scale = (wabs * rsr * dymax)[None, :, None]
+    z, _, _, _, _ = orc.bn_fwd_train(inp["x"], res_np, w_np, b_np, eps=eps, act="none", bf16=bf16)
+    dz = orc.widen(inp["dy"], bf16=bf16) * orc.act(act, z, grad=True, param=ap)
+    dx_scale = (wabs * rsr * np.abs(dz).max(axis=(0, 2)))[None, :, None]
     check(f"{tag} dx", to_f64(dx), rdx, dtype, group_axis=ch, report=report, scale=dx_scale)
     if residual:
         check(f"{tag} dres", to_f64(dres), rdres, dtype, group_axis=ch, report=report)
@@ -76,7 +89,7 @@ def run_case(orc, dtype, Nb, C, HW, act, residual, with_wb=True, eval_after=True
         # Eval reads the running statistics the training step just wrote
         # (float32 on the device, passed to the oracle as they stand).
         rye = orc.bn_fwd_eval(inp["x"], to_f64(rm), to_f64(rv), res_np, w_np, b_np, eps=eps,
-                              act=act, bf16=bf16)
+                              act=act, bf16=bf16, act_param=ap)
         check(f"{tag} y_eval", to_f64(ye), rye, dtype, group_axis=ch, report=report)
 
 
@@ -91,6 +104,29 @@ SMALL = [(2, 3, 5), (4, 8, 49), (3, 5, 1), (2, 4, 7), (5, 16, 64), (2, 2, 3136),
 def test_small_shapes(orc, dtype, act, residual, Nb, C, HW):
     print(f"case bn {dtype} {Nb}x{C}x{HW} {act} res={residual}", flush=True)
     run_case(orc, dtype, Nb, C, HW, act, residual)
+
+
+# The rest of the activation family, on the run-time-dispatched kernels.  The
+# weight is scaled by 4 so z spreads over about [-16, 16] and every branch
+# (both saturations of relu6 / hardsigmoid / hardswish, the exp tails) is hit.
+FAMILY = [("sigmoid", 0.0), ("tanh", 0.0), ("silu", 0.0), ("mish", 0.0), ("leaky_relu", 0.01),
+          ("leaky_relu", 0.2), ("elu", 1.0), ("elu", 0.5), ("selu", 0.0), ("celu", 1.0),
+          ("celu", 2.0), ("softplus", 0.0), ("relu6", 0.0), ("hardsigmoid", 0.0),
+          ("hardswish", 0.0)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("act,ap", FAMILY)
+@pytest.mark.parametrize("residual", [False, True])
+@pytest.mark.parametrize("Nb,C,HW", [(4, 8, 49), (7, 3, 1000), (2, 2, 3136)])
+def test_activation_family(orc, dtype, act, ap, residual, Nb, C, HW):
+    print(f"case bn {dtype} {Nb}x{C}x{HW} {act}({ap}) res={residual}", flush=True)
+    run_case(orc, dtype, Nb, C, HW, act, residual, act_param=ap, w_scale=4)
+
+
+def test_softplus_threshold(orc):
+    """z beyond 20 takes softplus's identity branch (weight scaled by 8)."""
+    run_case(orc, "f32", 4, 4, 2000, "softplus", True, w_scale=8)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -121,9 +157,12 @@ def test_backward_bitwise_deterministic(orc):
     x, res, w, b, dy = (to_dev(inp[k], "f32") for k in ("x", "res", "w", "b", "dy"))
     outs = []
     for _ in range(2):
-        rm = torch.zeros(32, device="cuda"); rv = torch.ones(32, device="cuda")
-        y, sm, sr = nl.bn_fwd_train(x, w, b, rm, rv, wl.eps, wl.momentum, "relu", res)
-        outs.append((y, sm, sr) + nl.bn_bwd(dy, x, w, b, sm, sr, "relu", res))
+        run = []
+        for act in ("relu", "mish"):
+            rm = torch.zeros(32, device="cuda"); rv = torch.ones(32, device="cuda")
+            y, sm, sr = nl.bn_fwd_train(x, w, b, rm, rv, wl.eps, wl.momentum, act, res)
+            run += [y, sm, sr, rm, rv] + list(nl.bn_bwd(dy, x, w, b, sm, sr, act, res))
+        outs.append(run)
     torch.cuda.synchronize()
     for a, b_ in zip(outs[0], outs[1]):
         assert torch.equal(a, b_)

@@ -77,8 +77,8 @@ def test_bn_closed_form(orc):
 def test_activation_table(orc):
     g = _golden("activations_table.json")
     for c in g["cases"]:
-        f = orc.act(c["act"], np.array([c["z"]]))[0]
-        df = orc.act(c["act"], np.array([c["z"]]), grad=True)[0]
+        f = orc.act(c["act"], np.array([c["z"]]), param=c.get("p", 0.0))[0]
+        df = orc.act(c["act"], np.array([c["z"]]), grad=True, param=c.get("p", 0.0))[0]
         assert f == pytest.approx(c["f"], rel=1e-14, abs=1e-15), c
         assert df == pytest.approx(c["df"], rel=1e-14, abs=1e-15), c
 
@@ -96,6 +96,44 @@ def test_gelu_limits_and_library(orc):
     zz = np.linspace(-5, 5, 101)
     fd = (orc.act("gelu", zz + h) - orc.act("gelu", zz - h)) / (2 * h)
     np.testing.assert_allclose(orc.act("gelu", zz, grad=True), fd, atol=1e-8)
+
+
+# Activation family against PyTorch float64 (values, derivatives by autograd,
+# and PyTorch's conventions at the kinks).  CELU takes alpha = 2: with an
+# alpha such as 0.8, PyTorch's float64 CELU gradient differs from the
+# definition by ~3e-7 relative (its 1/alpha input scale is not carried in
+# double precision), while alpha = 2 makes 1/alpha exact.
+TORCH_ACTS = {
+    "sigmoid": (lambda t, p: torch.sigmoid(t), 0.0),
+    "tanh": (lambda t, p: torch.tanh(t), 0.0),
+    "silu": (lambda t, p: F.silu(t), 0.0),
+    "mish": (lambda t, p: F.mish(t), 0.0),
+    "leaky_relu": (lambda t, p: F.leaky_relu(t, p), 0.07),
+    "elu": (lambda t, p: F.elu(t, p), 1.3),
+    "selu": (lambda t, p: F.selu(t), 0.0),
+    "celu": (lambda t, p: F.celu(t, p), 2.0),  # alpha exact in binary (see below)
+    "softplus": (lambda t, p: F.softplus(t), 0.0),
+    "relu6": (lambda t, p: F.relu6(t), 0.0),
+    "hardsigmoid": (lambda t, p: F.hardsigmoid(t), 0.0),
+    "hardswish": (lambda t, p: F.hardswish(t), 0.0),
+    "relu": (lambda t, p: F.relu(t), 0.0),
+    "gelu": (lambda t, p: F.gelu(t, approximate="none"), 0.0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TORCH_ACTS))
+def test_activation_family_matches_torch(orc, name):
+    fn, p = TORCH_ACTS[name]
+    # A grid with the kinks (0, +-3, 6, 20) on it, plus tails.
+    z = np.concatenate([np.linspace(-30, 30, 6001), [0.0, -3.0, 3.0, 6.0, 20.0, -20.0]])
+    t = torch.tensor(z, requires_grad=True)
+    y = fn(t, p)
+    y.sum().backward()
+    np.testing.assert_allclose(orc.act(name, z, param=p), y.detach().numpy(), rtol=1e-14, atol=1e-15)
+    # PyTorch's hardsigmoid gradient uses a float32 literal for 1/6.
+    rtol = 1e-7 if name == "hardsigmoid" else 1e-13
+    np.testing.assert_allclose(orc.act(name, z, grad=True, param=p), t.grad.numpy(), rtol=rtol,
+                               atol=1e-15)
 
 
 # ------------------------------------------------------------- invariants
@@ -260,7 +298,8 @@ def test_rms_finite_differences(orc):
 
 
 @pytest.mark.parametrize("act,res", [("relu", True), ("gelu", False), ("gelu", True),
-                                     ("none", False)])
+                                     ("none", False), ("silu", True), ("mish", False),
+                                     ("elu", True), ("tanh", False)])
 def test_bn_finite_differences(orc, act, res):
     rng = np.random.default_rng(10)
     shape = (2, 3, 5)
@@ -273,8 +312,9 @@ def test_bn_finite_differences(orc, act, res):
         _, sm, sr, _, _ = orc.bn_fwd_train(x, None, w, b, eps=eps)
         z = (x - sm[None, :, None]) * sr[None, :, None] * w[None, :, None] + b[None, :, None] + r
         r = r + np.where(np.abs(z) < 0.05, np.sign(z) * 0.1 + (z == 0) * 0.1, 0.0)
-    L = lambda: float((orc.bn_fwd_train(x, r, w, b, eps=eps, act=act)[0] * dy).sum())
-    dx, dres, dw, db = orc.bn_bwd(dy, x, r, w, b, eps=eps, act=act)
+    p = 1.3 if act == "elu" else 0.0
+    L = lambda: float((orc.bn_fwd_train(x, r, w, b, eps=eps, act=act, act_param=p)[0] * dy).sum())
+    dx, dres, dw, db = orc.bn_bwd(dy, x, r, w, b, eps=eps, act=act, act_param=p)
     np.testing.assert_allclose(dx, _fd(L, x), atol=2e-7)
     np.testing.assert_allclose(dw, _fd(L, w), atol=2e-7)
     np.testing.assert_allclose(db, _fd(L, b), atol=2e-7)
