@@ -110,15 +110,28 @@ def bytes_bn(wl, es):
 
 
 # ------------------------------------------------------------ workloads
+ELEM_SIZE = {"f32": 4, "bf16": 2, "f16": 2}
+
+
+def torch_dtype(torch, dtype):
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+
+
+def to_device(torch, a, dtype):
+    """Host array in the I/O representation (bf16 as uint16 bits) -> device."""
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
 class RowBench:
     def __init__(self, wl, nl, torch):
         from normalization_ln_rmsnorm_amd.workloads import gen_rowwise
         self.wl, self.nl, self.torch = wl, nl, torch
         M, N = wl.shape
         self.inp = gen_rowwise(wl)
-        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-        dev = lambda a: (torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-                         if wl.dtype == "bf16" else torch.from_numpy(a).cuda())
+        tdt = torch_dtype(torch, wl.dtype)
+        dev = lambda a: to_device(torch, a, wl.dtype)
         self.x, self.dy, self.w = dev(self.inp["x"]), dev(self.inp["dy"]), dev(self.inp["w"])
         self.b = dev(self.inp["b"]) if wl.kind == "ln" else None
         self.y = torch.empty(M, N, dtype=tdt, device="cuda")
@@ -129,7 +142,7 @@ class RowBench:
         self.db = torch.empty(N, dtype=tdt, device="cuda")
         ws_fn = nl.ln_bwd_workspace_bytes if wl.kind == "ln" else nl.rms_bwd_workspace_bytes
         self.ws = torch.empty(max(1, ws_fn(tdt, M, N)), dtype=torch.uint8, device="cuda")
-        self.bytes = bytes_rowwise(wl.kind, M, N, 2 if wl.dtype == "bf16" else 4)
+        self.bytes = bytes_rowwise(wl.kind, M, N, ELEM_SIZE[wl.dtype])
         self.ops = ["fwd", "bwd"]
         self.dominant = "bwd"
 
@@ -163,10 +176,9 @@ class BnBench:
         self.wl, self.nl, self.torch = wl, nl, torch
         Nb, C, H, W = wl.shape
         inp = gen_bn(wl)
-        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        tdt = torch_dtype(torch, wl.dtype)
         shape = (Nb, C, H, W)
-        dev = lambda a: (torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
-                         if wl.dtype == "bf16" else torch.from_numpy(a).cuda())
+        dev = lambda a: to_device(torch, a, wl.dtype)
         self.x = dev(inp["x"]).view(shape)
         self.dy = dev(inp["dy"]).view(shape)
         self.res = dev(inp["res"]).view(shape) if wl.residual else None
@@ -183,7 +195,7 @@ class BnBench:
         self.dw = torch.empty(C, dtype=tdt, device="cuda")
         self.db = torch.empty(C, dtype=tdt, device="cuda")
         self.ws = torch.empty(nl.bn_workspace_bytes(tdt, Nb, C, H * W), dtype=torch.uint8, device="cuda")
-        self.bytes = bytes_bn(wl, 2 if wl.dtype == "bf16" else 4)
+        self.bytes = bytes_bn(wl, ELEM_SIZE[wl.dtype])
         self.ops = ["fwd", "bwd"] + (["eval"] if wl.eval_after_train else [])
         self.dominant = "bwd"
 
@@ -343,7 +355,7 @@ def main():
         sys.exit(2)
     import torch
     import normalization_ln_rmsnorm_amd as nl
-    from normalization_ln_rmsnorm_amd.workloads import HEADLINE, WORKLOADS
+    from normalization_ln_rmsnorm_amd.workloads import EXTRA_WORKLOADS, HEADLINE, WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -354,7 +366,8 @@ def main():
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
 
     name = args.workload or HEADLINE
-    wl = WORKLOADS[name]
+    every = {**WORKLOADS, **EXTRA_WORKLOADS}
+    wl = every[name]
     mk = RowBench if wl.kind in ("ln", "rms") else BnBench
     bench = mk(wl, nl, torch)
     meas = measure(bench, args.steps, args.warmup, torch, hip, nl, flush)
@@ -365,10 +378,10 @@ def main():
 
     per = {}
     if not args.no_others:
-        for other in WORKLOADS:
+        for other in every:
             if other == name:
                 continue
-            ow = WORKLOADS[other]
+            ow = every[other]
             b = (RowBench if ow.kind in ("ln", "rms") else BnBench)(ow, nl, torch)
             per[other] = summarize(b, measure(b, args.other_steps, 3, torch, hip, nl, flush))
             print(f"[bench] {other}: " + "  ".join(

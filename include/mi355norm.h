@@ -22,10 +22,11 @@
  *   Tensors may have any alignment; 16-byte aligned tensors whose rows (or
  *   planes) are a multiple of 16 bytes take the 128-bit vector path.
  * Dtypes.  `dt` is the I/O dtype of x, y, dy, dx, res, dres, w, b, dw, db:
- *   NORM_F32 (float) or NORM_BF16 (bfloat16 bit patterns).  Statistics
- *   (mean, rstd, save_*, running_*) are always float32.  All arithmetic is
- *   float32 with float64 for cross-workgroup merges; bf16 results are
- *   rounded to nearest-even once, at the store.
+ *   NORM_F32 (float), NORM_BF16 (bfloat16 bit patterns) or NORM_F16 (IEEE
+ *   binary16 bit patterns).  Statistics (mean, rstd, save_*, running_*) are
+ *   always float32.  All arithmetic is float32 with float64 for
+ *   cross-workgroup merges; 16-bit results are rounded to nearest-even
+ *   once, at the store (fp16 results beyond its range become +-inf).
  * Streams.  `stream` is a hipStream_t (NULL = the legacy default stream).
  *   Kernels are enqueued on it and the call returns without synchronizing.
  * Ownership.  The caller allocates and owns every buffer, including the
@@ -62,7 +63,7 @@ typedef enum {
     NORM_ERR_HIP = -7        /* the HIP runtime rejected a launch           */
 } norm_status;
 
-typedef enum { NORM_F32 = 0, NORM_BF16 = 1 } norm_dtype;
+typedef enum { NORM_F32 = 0, NORM_BF16 = 1, NORM_F16 = 2 } norm_dtype;
 
 /* Activation fused after BatchNorm ([NormPage] "BatchNorm" section: relu,
  * gelu, silu, mish, leaky_relu and a dozen more; [ActPage] sections 5-6).
@@ -87,8 +88,9 @@ typedef enum {
 } norm_act;
 
 /* Largest row width the row-wise kernels accept (rows are held in
- * registers): 65536 features for bf16, 32768 for float32. */
-#define NORM_MAX_N_BF16 65536
+ * registers): 65536 features for the 16-bit dtypes, 32768 for float32. */
+#define NORM_MAX_N_16 65536
+#define NORM_MAX_N_BF16 NORM_MAX_N_16
 #define NORM_MAX_N_F32 32768
 
 /* ------------------------------------------------------------- LayerNorm

@@ -248,7 +248,7 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
                 BnGeom g, int act_rt, float act_p) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
-    constexpr bool kFast = sizeof(T) == 2;
+    constexpr bool kFast = std::is_same<T, bf16_t>::value;  // fp16 keeps the exact forms
     int c; int64_t n0, n1;
     tile_of_block(g, &c, &n0, &n1);
     float mean, rstd;
@@ -359,7 +359,7 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
                         if (ACT != kActNone) {
                             float z = fmaf(xf[e], a, s);
                             if (RES) z += rf[e];
-                            dz[e] = df[e] * act_grad_any<ACT, !kExact>(z, act_rt, act_p);
+                            dz[e] = df[e] * act_grad_any<ACT, std::is_same<T, bf16_t>::value>(z, act_rt, act_p);
                         } else {
                             dz[e] = df[e];
                         }
@@ -449,7 +449,7 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
                  T *__restrict__ dx, BnGeom g, int act_rt, float act_p) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
-    constexpr bool kFast = sizeof(T) == 2;
+    constexpr bool kFast = std::is_same<T, bf16_t>::value;  // fp16 keeps the exact forms
     int c; int64_t n0, n1;
     tile_of_block(g, &c, &n0, &n1);
     double sums[3];
@@ -628,7 +628,7 @@ static void launch_bwd_act(const BnGeom &g, hipStream_t st, bool has_res, int ac
         launch("bn_bwd_reduce_kernel", false, bn_bwd_reduce_kernel<T, V, ACT, false>, grid, blk, 0, st,
                (const T *)dy, (const T *)x, (const T *)res, (const T *)w, (const T *)b, sm, sr, (T *)dres, g, part,
                act_rt, act_p);
-    // dz for pass 2: float32 dres holds dz exactly; bf16 dres is rounded, so
+    // dz for pass 2: float32 dres holds dz exactly; 16-bit dres is rounded, so
     // there dz is recomputed from dy and x (and res).
     const bool fp32 = sizeof(T) == 4;
     const bool main = !has_res;
@@ -701,11 +701,12 @@ extern "C" norm_status bn_fwd_train(norm_dtype dt, int64_t Nb, int64_t C, int64_
     const BnGeom g = make_geom(dt, Nb, C, HW);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool vec = bn_vec_ok(dt, HW, {x, res, y});
-    if (dt == NORM_F32)
-        return vec ? launch_fwd_train<float, 4>(g, st, act, act_param, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws)
-                   : launch_fwd_train<float, 1>(g, st, act, act_param, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws);
-    return vec ? launch_fwd_train<bf16_t, 8>(g, st, act, act_param, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws)
-               : launch_fwd_train<bf16_t, 1>(g, st, act, act_param, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws);
+    return with_io_type(dt, [&](auto tag) {
+        using T = typename decltype(tag)::type;
+        constexpr int VW = 16 / (int)sizeof(T);
+        return vec ? launch_fwd_train<T, VW>(g, st, act, act_param, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws)
+                   : launch_fwd_train<T, 1>(g, st, act, act_param, eps, momentum, x, res, w, b, running_mean, running_var, save_mean, save_rstd, y, ws);
+    });
 }
 
 extern "C" norm_status bn_fwd_eval(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, float eps, norm_act act,
@@ -721,11 +722,12 @@ extern "C" norm_status bn_fwd_eval(norm_dtype dt, int64_t Nb, int64_t C, int64_t
     const BnGeom g = make_geom(dt, Nb, C, HW);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool vec = bn_vec_ok(dt, HW, {x, res, y});
-    if (dt == NORM_F32)
-        return vec ? launch_fwd_eval<float, 4>(g, st, act, act_param, eps, x, res, w, b, running_mean, running_var, y)
-                   : launch_fwd_eval<float, 1>(g, st, act, act_param, eps, x, res, w, b, running_mean, running_var, y);
-    return vec ? launch_fwd_eval<bf16_t, 8>(g, st, act, act_param, eps, x, res, w, b, running_mean, running_var, y)
-               : launch_fwd_eval<bf16_t, 1>(g, st, act, act_param, eps, x, res, w, b, running_mean, running_var, y);
+    return with_io_type(dt, [&](auto tag) {
+        using T = typename decltype(tag)::type;
+        constexpr int VW = 16 / (int)sizeof(T);
+        return vec ? launch_fwd_eval<T, VW>(g, st, act, act_param, eps, x, res, w, b, running_mean, running_var, y)
+                   : launch_fwd_eval<T, 1>(g, st, act, act_param, eps, x, res, w, b, running_mean, running_var, y);
+    });
 }
 
 extern "C" norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, norm_act act, float act_param,
@@ -746,9 +748,10 @@ extern "C" norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, 
     const BnGeom g = make_geom(dt, Nb, C, HW);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool vec = bn_vec_ok(dt, HW, {dy, x, res, dx, dres});
-    if (dt == NORM_F32)
-        return vec ? launch_bwd<float, 4>(g, st, act, act_param, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws)
-                   : launch_bwd<float, 1>(g, st, act, act_param, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws);
-    return vec ? launch_bwd<bf16_t, 8>(g, st, act, act_param, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws)
-               : launch_bwd<bf16_t, 1>(g, st, act, act_param, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws);
+    return with_io_type(dt, [&](auto tag) {
+        using T = typename decltype(tag)::type;
+        constexpr int VW = 16 / (int)sizeof(T);
+        return vec ? launch_bwd<T, VW>(g, st, act, act_param, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws)
+                   : launch_bwd<T, 1>(g, st, act, act_param, dy, x, res, w, b, save_mean, save_rstd, dx, dres, dw, db, ws);
+    });
 }

@@ -1,5 +1,5 @@
 // norm_device.hpp -- device-side building blocks for the gfx950 kernels:
-// element I/O (float32 / bf16, 128-bit vectors), wave64 reductions (DPP,
+// element I/O (float32 / bf16 / fp16, 128-bit vectors), wave64 reductions (DPP,
 // ds_swizzle, readlane), and the activation functions.
 //
 // [ActPage] = "Operator fusion in practice: attorch's activation and dropout
@@ -21,7 +21,15 @@ struct bf16_t {
     uint16_t bits;
 };
 
+// fp16 (IEEE binary16) likewise travels as its bit pattern; widening is exact
+// and narrowing rounds to nearest-even (the hardware conversion in the
+// default rounding mode).
+struct f16_t {
+    uint16_t bits;
+};
+
 typedef __bf16 hw_bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 hw_f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float hw_f32x2 __attribute__((ext_vector_type(2)));
 
@@ -31,6 +39,21 @@ __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     hw_f32x2 v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, hw_bf16x2));
+}
+
+__device__ __forceinline__ void unpack_f16x2(uint32_t u, float *f) {
+    const hw_f32x2 v = __builtin_convertvector(__builtin_bit_cast(hw_f16x2, u), hw_f32x2);
+    f[0] = v.x;
+    f[1] = v.y;
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    hw_f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, hw_f16x2));
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
 }
 
 // Vec<T, V>: V consecutive elements of type T moved by one load/store
@@ -82,6 +105,28 @@ template <> struct Vec<bf16_t, 1> {
     }
 };
 
+template <> struct Vec<f16_t, 8> {
+    static constexpr int n = 8;
+    using raw_t = u32x4;
+    __device__ __forceinline__ static void unpack(const raw_t &r, float *f) {
+        unpack_f16x2(r.x, f); unpack_f16x2(r.y, f + 2);
+        unpack_f16x2(r.z, f + 4); unpack_f16x2(r.w, f + 6);
+    }
+    __device__ __forceinline__ static raw_t pack(const float *f) {
+        return raw_t{pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]),
+                     pack_f16x2(f[4], f[5]), pack_f16x2(f[6], f[7])};
+    }
+};
+
+template <> struct Vec<f16_t, 1> {
+    static constexpr int n = 1;
+    using raw_t = uint16_t;
+    __device__ __forceinline__ static void unpack(const raw_t &r, float *f) { f[0] = f16_to_f32(r); }
+    __device__ __forceinline__ static raw_t pack(const float *f) {
+        return raw_t(pack_f16x2(f[0], 0.0f) & 0xffffu);
+    }
+};
+
 // Vector loads and stores.  `p` points at element 0 of the vector.
 template <typename T, int V>
 __device__ __forceinline__ typename Vec<T, V>::raw_t vload(const T *p) {
@@ -106,6 +151,8 @@ __device__ __forceinline__ float ld1(const float *p) { return *p; }
 __device__ __forceinline__ float ld1(const bf16_t *p) { return __uint_as_float(uint32_t(p->bits) << 16); }
 __device__ __forceinline__ void st1(float *p, float v) { *p = v; }
 __device__ __forceinline__ void st1(bf16_t *p, float v) { p->bits = uint16_t(pack_bf16x2(v, 0.0f) & 0xffffu); }
+__device__ __forceinline__ float ld1(const f16_t *p) { return f16_to_f32(p->bits); }
+__device__ __forceinline__ void st1(f16_t *p, float v) { p->bits = uint16_t(pack_f16x2(v, 0.0f) & 0xffffu); }
 
 // ------------------------------------------------------- wave reductions
 // DPP control codes (gfx9 encoding).

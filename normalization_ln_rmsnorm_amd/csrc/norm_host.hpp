@@ -8,13 +8,26 @@
 #include <stdint.h>
 
 #include "../../include/mi355norm.h"
+#include "norm_device.hpp"
 
 namespace mi355norm {
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-inline size_t dtype_size(norm_dtype dt) { return dt == NORM_BF16 ? 2 : 4; }
-inline bool dtype_ok(norm_dtype dt) { return dt == NORM_F32 || dt == NORM_BF16; }
+inline size_t dtype_size(norm_dtype dt) { return dt == NORM_F32 ? 4 : 2; }
+inline bool dtype_ok(norm_dtype dt) { return dt == NORM_F32 || dt == NORM_BF16 || dt == NORM_F16; }
+
+// Calls f(type_tag<T>{}) with T the element type of a (checked) I/O dtype.
+template <typename T> struct type_tag { using type = T; };
+
+template <typename F>
+inline auto with_io_type(norm_dtype dt, F &&f) {
+    switch (dt) {
+    case NORM_F32: return f(type_tag<float>{});
+    case NORM_BF16: return f(type_tag<bf16_t>{});
+    default: return f(type_tag<f16_t>{});
+    }
+}
 
 // Compute units of the current device (cached per device id).
 int device_cu_count();

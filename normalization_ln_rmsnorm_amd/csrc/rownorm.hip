@@ -597,7 +597,7 @@ static bool row_vec_ok(norm_dtype dt, int64_t N, std::initializer_list<const voi
 static norm_status check_rows(norm_dtype dt, int64_t M, int64_t N) {
     if (!dtype_ok(dt)) return NORM_ERR_DTYPE;
     if (M < 0 || N < 1) return NORM_ERR_SHAPE;
-    if (N > (dt == NORM_BF16 ? NORM_MAX_N_BF16 : NORM_MAX_N_F32)) return NORM_ERR_SHAPE;
+    if (N > (dt == NORM_F32 ? NORM_MAX_N_F32 : NORM_MAX_N_16)) return NORM_ERR_SHAPE;
     if (M > (int64_t)1 << 40) return NORM_ERR_SHAPE;
     return NORM_OK;
 }
@@ -617,11 +617,12 @@ static norm_status fwd_entry(norm_dtype dt, int64_t M, int64_t N, float eps, con
     RowPlan p;
     if (!make_plan(dt, M, N, vec, false, &p)) return NORM_ERR_SHAPE;
     const int n = (int)N;
-    if (dt == NORM_F32)
-        return vec ? launch_fwd_v<float, RMS, 4>(p, s, x, w, b, y, mean, rstd, M, n, eps)
-                   : launch_fwd_v<float, RMS, 1>(p, s, x, w, b, y, mean, rstd, M, n, eps);
-    return vec ? launch_fwd_v<bf16_t, RMS, 8>(p, s, x, w, b, y, mean, rstd, M, n, eps)
-               : launch_fwd_v<bf16_t, RMS, 1>(p, s, x, w, b, y, mean, rstd, M, n, eps);
+    return with_io_type(dt, [&](auto tag) {
+        using T = typename decltype(tag)::type;
+        constexpr int VW = 16 / (int)sizeof(T);
+        return vec ? launch_fwd_v<T, RMS, VW>(p, s, x, w, b, y, mean, rstd, M, n, eps)
+                   : launch_fwd_v<T, RMS, 1>(p, s, x, w, b, y, mean, rstd, M, n, eps);
+    });
 }
 
 static size_t bwd_ws_bytes(norm_dtype dt, int64_t M, int64_t N, int nparts) {
@@ -651,10 +652,11 @@ static norm_status bwd_entry(norm_dtype dt, int64_t M, int64_t N, const void *dy
         const dim3 grid((unsigned)ceil_div(N, 256));
         for (void *out : {dw, db}) {
             if (!out) continue;
-            if (dt == NORM_F32)
-                launch("zero_fill_kernel", false, zero_fill_kernel<float>, grid, dim3(256), 0, s, (float *)out, n);
-            else
-                launch("zero_fill_kernel", false, zero_fill_kernel<bf16_t>, grid, dim3(256), 0, s, (bf16_t *)out, n);
+            with_io_type(dt, [&](auto tag) {
+                using T = typename decltype(tag)::type;
+                launch("zero_fill_kernel", false, zero_fill_kernel<T>, grid, dim3(256), 0, s, (T *)out, n);
+                return 0;
+            });
         }
         return launch_status();
     }
@@ -663,22 +665,18 @@ static norm_status bwd_entry(norm_dtype dt, int64_t M, int64_t N, const void *dy
     if (!make_plan(dt, M, N, vec, true, &p)) return NORM_ERR_SHAPE;
     float *part_w = dw ? static_cast<float *>(ws) : nullptr;
     float *part_b = (!RMS && db) ? static_cast<float *>(ws) + (size_t)max_partial_rows(M) * N : nullptr;
-    if (dt == NORM_F32)
-        st = vec ? launch_bwd_v<float, RMS, 4>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n)
-                 : launch_bwd_v<float, RMS, 1>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n);
-    else
-        st = vec ? launch_bwd_v<bf16_t, RMS, 8>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n)
-                 : launch_bwd_v<bf16_t, RMS, 1>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n);
-    if (st != NORM_OK || !want) return st;
-    dim3 grid((unsigned)ceil_div(N, kColsumCols), RMS ? 1 : 2);
-    dim3 block(kColsumCols, kColsumSlices);
-    if (dt == NORM_F32)
-        launch("colsum_kernel", false, colsum_kernel<float>, grid, block, 0, s, (const float *)part_w,
-               (const float *)part_b, p.grid, n, (float *)dw, (float *)db);
-    else
-        launch("colsum_kernel", false, colsum_kernel<bf16_t>, grid, block, 0, s, (const float *)part_w,
-               (const float *)part_b, p.grid, n, (bf16_t *)dw, (bf16_t *)db);
-    return launch_status();
+    return with_io_type(dt, [&](auto tag) {
+        using T = typename decltype(tag)::type;
+        constexpr int VW = 16 / (int)sizeof(T);
+        norm_status r = vec ? launch_bwd_v<T, RMS, VW>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n)
+                            : launch_bwd_v<T, RMS, 1>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n);
+        if (r != NORM_OK || !want) return r;
+        dim3 grid((unsigned)ceil_div(N, kColsumCols), RMS ? 1 : 2);
+        dim3 block(kColsumCols, kColsumSlices);
+        launch("colsum_kernel", false, colsum_kernel<T>, grid, block, 0, s, (const float *)part_w,
+               (const float *)part_b, p.grid, n, (T *)dw, (T *)db);
+        return launch_status();
+    });
 }
 
 }  // namespace mi355norm

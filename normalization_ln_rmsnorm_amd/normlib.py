@@ -7,7 +7,7 @@ an exception is raised.
 
 Functions keep the C names (ln_fwd, ln_bwd, rms_fwd, rms_bwd, bn_fwd_train,
 bn_fwd_eval, bn_bwd).  Tensors must be contiguous CUDA (HIP) tensors of
-dtype float32 or bfloat16; statistics are float32.  Outputs that are not
+dtype float32, bfloat16 or float16; statistics are float32.  Outputs that are not
 passed in are allocated with torch.
 """
 import ctypes
@@ -18,7 +18,7 @@ import torch  # loaded first so the library binds to torch's HIP runtime
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmi355norm.so")
 
-NORM_F32, NORM_BF16 = 0, 1
+NORM_F32, NORM_BF16, NORM_F16 = 0, 1, 2
 ACT = {"none": 0, "relu": 1, "gelu": 2, "sigmoid": 3, "tanh": 4, "silu": 5, "mish": 6,
        "leaky_relu": 7, "elu": 8, "selu": 9, "celu": 10, "softplus": 11, "relu6": 12,
        "hardsigmoid": 13, "hardswish": 14}
@@ -88,7 +88,9 @@ def _dt(t):
         return NORM_F32
     if t.dtype == torch.bfloat16:
         return NORM_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+    if t.dtype == torch.float16:
+        return NORM_F16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32, bfloat16 or float16")
 
 
 def _ptr(t):

@@ -8,7 +8,8 @@ seeded per workload, in a fixed draw order:
     x, per-channel parameters, outlier columns, weight, bias, residual, dy.
 
 Values are drawn in float32; bf16 workloads round each float32 value to the
-nearest bf16 (ties to even) once and hand out the 16-bit patterns as uint16.
+nearest bf16 (ties to even) once and hand out the 16-bit patterns as uint16;
+fp16 variants (same recipe, dtype "f16") round to float16 arrays.
 "N(a, s)" means mean a, standard deviation s.
 
 The six workloads (sizes as the benchmark runs them):
@@ -47,7 +48,7 @@ import numpy as np
 class Workload:
     name: str
     kind: str            # "ln", "rms" or "bn"
-    dtype: str           # "f32" or "bf16" (I/O dtype)
+    dtype: str           # "f32", "bf16" or "f16" (I/O dtype)
     shape: tuple         # (M, N) for ln/rms, (N, C, H, W) for bn
     seed: int
     eps: float
@@ -89,6 +90,22 @@ WORKLOADS = {
 HEADLINE = "rms_bf16_16384x4096"
 
 
+def _variant(base: str, name: str, **changes) -> Workload:
+    from dataclasses import replace
+    return replace(WORKLOADS[base], name=name, **changes)
+
+
+# Variants beyond the six above, measured alongside them: the same recipes
+# with fp16 I/O.
+EXTRA_WORKLOADS = {
+    w.name: w
+    for w in [
+        _variant("rms_bf16_16384x4096", "rms_f16_16384x4096", dtype="f16"),
+        _variant("bn_bf16_256x64x112x112", "bn_f16_256x64x112x112", dtype="f16"),
+    ]
+}
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even); uint16 bits.
 
@@ -98,9 +115,16 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return ((u + bias) >> np.uint32(16)).astype(np.uint16)
 
 
-def _cast(a: np.ndarray, dtype: str) -> np.ndarray:
+def to_io(a: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values -> the I/O representation: float32, bf16 bits (uint16)
+    or float16, each rounded to nearest-even."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    return f32_to_bf16_bits(a) if dtype == "bf16" else a
+    if dtype == "bf16":
+        return f32_to_bf16_bits(a)
+    if dtype == "f16":
+        return a.astype(np.float16)
+    return a
+
 
 
 def _normal(rng, size, mean=0.0, std=1.0):
@@ -116,7 +140,7 @@ def gen_rowwise(wl: Workload, M: int = None, N: int = None, seed: int = None):
     """Inputs for a LayerNorm / RMSNorm workload, optionally at another shape.
 
     Returns dict(x, w, b, dy) (b is None for RMSNorm) in the workload's I/O
-    dtype (float32 arrays, or uint16 bf16 bit patterns)."""
+    dtype (float32 arrays, uint16 bf16 bit patterns, or float16 arrays)."""
     M = wl.shape[0] if M is None else M
     N = wl.shape[1] if N is None else N
     rng = np.random.default_rng(wl.seed if seed is None else seed)
@@ -132,8 +156,8 @@ def gen_rowwise(wl: Workload, M: int = None, N: int = None, seed: int = None):
         w = np.float32(1.0) + _normal(rng, (N,), std=0.1)
         b = _normal(rng, (N,), std=0.1)
     dy = _normal(rng, (M, N))
-    out = dict(x=_cast(x, wl.dtype), w=_cast(w, wl.dtype), dy=_cast(dy, wl.dtype),
-               b=_cast(b, wl.dtype) if b is not None else None)
+    out = dict(x=to_io(x, wl.dtype), w=to_io(w, wl.dtype), dy=to_io(dy, wl.dtype),
+               b=to_io(b, wl.dtype) if b is not None else None)
     return out
 
 
@@ -157,6 +181,6 @@ def gen_bn(wl: Workload, Nb: int = None, C: int = None, HW: int = None, seed: in
     b = _normal(rng, (C,), std=0.1)
     res = _normal(rng, (Nb, C, HW)) if wl.residual else None
     dy = _normal(rng, (Nb, C, HW))
-    return dict(x=_cast(x, wl.dtype), res=_cast(res, wl.dtype) if res is not None else None,
-                w=_cast(w, wl.dtype), b=_cast(b, wl.dtype), dy=_cast(dy, wl.dtype),
+    return dict(x=to_io(x, wl.dtype), res=to_io(res, wl.dtype) if res is not None else None,
+                w=to_io(w, wl.dtype), b=to_io(b, wl.dtype), dy=to_io(dy, wl.dtype),
                 running_mean=np.zeros(C, np.float32), running_var=np.ones(C, np.float32))

@@ -3,8 +3,9 @@
 Tolerances (fixed for the normalization family):
   float32 I/O  every element satisfies |got - ref| <= 1e-5 + 1e-5 * |ref|
                (statistics, running statistics and parameter gradients too);
-  bf16 I/O     every element satisfies |got - ref| <= 2 ulp_bf16(max(|ref|, F))
-               with ulp_bf16(v) = 2^(floor(log2 v) - 7) and the floor
+  bf16 / fp16  every element satisfies |got - ref| <= 2 ulp(max(|ref|, F))
+  I/O          with ulp_bf16(v) = 2^(floor(log2 v) - 7),
+               ulp_f16(v) = 2^(max(floor(log2 v), -14) - 10), and the floor
                F = 2^-12 * max(largest |ref| of that row, channel or vector,
                                the scale of the terms the output is formed
                                from, when given -- e.g. rstd * |dy * w| for
@@ -24,18 +25,24 @@ F32_RTOL = 1e-5
 BF16_ULPS = 2.0
 
 
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
 def to_dev(a, dtype, device="cuda"):
-    """numpy float32 array or uint16 bf16 bits -> device tensor."""
+    """numpy float32 array, uint16 bf16 bits or float16 array -> device tensor."""
     if a is None:
         return None
     if dtype == "bf16":
         assert a.dtype == np.uint16
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    if dtype == "f16":
+        assert a.dtype == np.float16
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
 def to_f64(t):
-    """Device tensor (float32 or bf16) -> exact float64 numpy array."""
+    """Device tensor (float32, bf16 or fp16) -> exact float64 numpy array."""
     if t.dtype == torch.bfloat16:
         bits = t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
         return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
@@ -45,6 +52,11 @@ def to_f64(t):
 def ulp_bf16(v):
     v = np.maximum(np.abs(v), np.finfo(np.float64).tiny)
     return np.exp2(np.floor(np.log2(v)) - 7.0)
+
+
+def ulp_f16(v):
+    v = np.maximum(np.abs(v), np.finfo(np.float64).tiny)
+    return np.exp2(np.maximum(np.floor(np.log2(v)), -14.0) - 10.0)
 
 
 def check(name, got, ref, dtype, group_axis=None, report=None, scale=None):
@@ -70,10 +82,11 @@ def check(name, got, ref, dtype, group_axis=None, report=None, scale=None):
             R = np.abs(ref).max(axis=group_axis, keepdims=True, initial=0)
         if scale is not None:
             R = np.maximum(R, np.abs(scale))
+        ulp = ulp_bf16 if dtype == "bf16" else ulp_f16
         floor = np.exp2(-12.0) * R
-        u = ulp_bf16(np.maximum(np.abs(ref), floor))
+        u = ulp(np.maximum(np.abs(ref), floor))
         bad = err > BF16_ULPS * u
-        strict = err / ulp_bf16(ref)
+        strict = err / ulp(ref)
         summary = dict(name=name, max_ulp=float((err / u).max(initial=0)),
                        max_strict_ulp=float(strict.max(initial=0)),
                        n_strict_over_2=int((strict > 2).sum()), n_bad=int(bad.sum()))
@@ -90,6 +103,12 @@ def round_bf16_f32(a):
     """float32 array -> bf16 bits (nearest-even), for test-side input edits."""
     from normalization_ln_rmsnorm_amd.workloads import f32_to_bf16_bits
     return f32_to_bf16_bits(a)
+
+
+def to_io(a, dtype):
+    """float32 values -> the I/O representation of `dtype` (nearest-even)."""
+    from normalization_ln_rmsnorm_amd.workloads import to_io as _to_io
+    return _to_io(a, dtype)
 
 
 # Pre-activation values where an activation's derivative jumps (PyTorch's
@@ -114,7 +133,7 @@ def avoid_kinks(orc, inp, dtype, eps, act, delta=1e-3, step=None):
     if kinks.size == 0:
         return out, 0
     bf16 = dtype == "bf16"
-    step = step if step is not None else (0.0625 if bf16 else 4 * delta)
+    step = step if step is not None else {"bf16": 0.0625, "f16": 1.0 / 64}.get(dtype, 4 * delta)
     moved = 0
     for _ in range(6):
         y, _, _, _, _ = orc.bn_fwd_train(out["x"], out["res"], out["w"], out["b"], eps=eps,
@@ -130,7 +149,7 @@ def avoid_kinks(orc, inp, dtype, eps, act, delta=1e-3, step=None):
         key = "res" if out["res"] is not None else "x"
         base = orc.widen(out[key], bf16=bf16)
         edited = (base + np.where(near, shift, 0.0)).astype(np.float32)
-        out[key] = round_bf16_f32(edited) if bf16 else edited
+        out[key] = to_io(edited, dtype)
     raise AssertionError(f"could not move the pre-activations away from the {act} kinks")
 
 

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mi355norm.h")
 
 OK, ENULL, ESHAPE, EDTYPE, EACT, EARG, EWS = 0, -1, -2, -3, -4, -5, -6
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 P = ctypes.c_void_p(4096)  # a non-NULL pointer that validation must reject before use
 NULL = None
 
@@ -65,6 +65,9 @@ def test_row_errors(lib):
     assert lib.ln_fwd(F32, -1, 8, 1e-5, P, NULL, NULL, P, NULL, NULL, NULL) == ESHAPE
     assert lib.ln_fwd(F32, 4, 32769, 1e-5, P, NULL, NULL, P, NULL, NULL, NULL) == ESHAPE
     assert lib.ln_fwd(BF16, 4, 65537, 1e-5, P, NULL, NULL, P, NULL, NULL, NULL) == ESHAPE
+    assert lib.ln_fwd(F16, 4, 65537, 1e-5, P, NULL, NULL, P, NULL, NULL, NULL) == ESHAPE
+    assert lib.ln_fwd(3, 4, 8, 1e-5, P, NULL, NULL, P, NULL, NULL, NULL) == EDTYPE
+    assert lib.rms_bwd_workspace_bytes(F16, 4, 8) == lib.rms_bwd_workspace_bytes(BF16, 4, 8)
     assert lib.ln_fwd(F32, 4, 8, -1.0, P, NULL, NULL, P, NULL, NULL, NULL) == EARG
     assert lib.ln_fwd(F32, 4, 8, float("nan"), P, NULL, NULL, P, NULL, NULL, NULL) == EARG
     assert lib.ln_fwd(F32, 4, 8, 1e-5, NULL, NULL, NULL, P, NULL, NULL, NULL) == ENULL
@@ -100,6 +103,7 @@ def test_bn_errors(lib):
                                 a["sm"], a["sr"], a["y"], a["ws"], a["wsb"], a["s"])
 
     assert train(dt=4) == EDTYPE
+    assert train(dt=3) == EDTYPE
     assert train(act=15) == EACT
     assert train(act=-1) == EACT
     assert train(act=10, ap=0.0) == EARG    # CELU divides by its alpha

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests._parity import avoid_kinks, check, round_bf16_f32, to_dev, to_f64
+from tests._parity import avoid_kinks, check, to_dev, to_f64, to_io
 
 pytestmark = pytest.mark.gpu
 
@@ -21,14 +21,14 @@ from normalization_ln_rmsnorm_amd.workloads import WORKLOADS, gen_bn  # noqa: E4
 
 def _wl(dtype, act, residual):
     base = WORKLOADS["bn_f32_64x256x56x56"] if dtype == "f32" else WORKLOADS["bn_bf16_256x64x112x112"]
-    return dataclasses.replace(base, act=act, residual=residual)
+    return dataclasses.replace(base, dtype=dtype, act=act, residual=residual)
 
 
 def _scale_w(orc, inp, dtype, k):
-    """Multiply the affine weight by a power of two (exact in both formats)."""
+    """Multiply the affine weight by a power of two (exact in every format)."""
     out = dict(inp)
     w = orc.widen(inp["w"], bf16=dtype == "bf16") * k
-    out["w"] = round_bf16_f32(w.astype(np.float32)) if dtype == "bf16" else w.astype(np.float32)
+    out["w"] = to_io(w.astype(np.float32), dtype)
     return out
 
 
@@ -97,7 +97,7 @@ SMALL = [(2, 3, 5), (4, 8, 49), (3, 5, 1), (2, 4, 7), (5, 16, 64), (2, 2, 3136),
          (1, 2, 12544), (16, 4, 24)]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("act,residual", [("none", False), ("relu", True), ("gelu", False),
                                           ("gelu", True), ("relu", False), ("none", True)])
 @pytest.mark.parametrize("Nb,C,HW", SMALL)
@@ -115,7 +115,7 @@ FAMILY = [("sigmoid", 0.0), ("tanh", 0.0), ("silu", 0.0), ("mish", 0.0), ("leaky
           ("hardswish", 0.0)]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("act,ap", FAMILY)
 @pytest.mark.parametrize("residual", [False, True])
 @pytest.mark.parametrize("Nb,C,HW", [(4, 8, 49), (7, 3, 1000), (2, 2, 3136)])
@@ -129,7 +129,7 @@ def test_softplus_threshold(orc):
     run_case(orc, "f32", 4, 4, 2000, "softplus", True, w_scale=8)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_no_affine(orc, dtype):
     run_case(orc, dtype, 4, 6, 50, "gelu", True, with_wb=False)
 
@@ -147,6 +147,17 @@ def test_full_size_workloads(orc, name):
     report = []
     run_case(orc, wl.dtype, Nb, C, H * W, wl.act, wl.residual, eval_after=True, report=report,
              wl=wl)
+    for r in report:
+        print(r, flush=True)
+
+
+def test_full_size_f16(orc):
+    """The bf16 BatchNorm workload's recipe and shape with fp16 I/O."""
+    wl = dataclasses.replace(WORKLOADS["bn_bf16_256x64x112x112"], dtype="f16")
+    Nb, C, H, W = wl.shape
+    print("case bn f16 256x64x112x112 gelu", flush=True)
+    report = []
+    run_case(orc, "f16", Nb, C, H * W, wl.act, wl.residual, report=report, wl=wl)
     for r in report:
         print(r, flush=True)
 

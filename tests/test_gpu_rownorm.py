@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests._parity import check, to_dev, to_f64
+from tests._parity import TORCH_DTYPE, check, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,9 @@ def _wl(kind, dtype):
     """The workload whose value recipe a small case borrows."""
     if kind == "rms":
         return dataclasses.replace(WORKLOADS["rms_bf16_16384x4096"], dtype=dtype)
-    return WORKLOADS["ln_bf16_25216x768"] if dtype == "bf16" else WORKLOADS["ln_f32_64x256"]
+    if dtype == "f32":
+        return WORKLOADS["ln_f32_64x256"]
+    return dataclasses.replace(WORKLOADS["ln_bf16_25216x768"], dtype=dtype)
 
 
 def run_case(orc, kind, dtype, M, N, with_w=True, with_b=True, eps=None, seed=None, guard=True,
@@ -46,7 +48,7 @@ def run_case(orc, kind, dtype, M, N, with_w=True, with_b=True, eps=None, seed=No
     eps = wl.eps if eps is None else eps
     inp = gen_rowwise(wl, M=M, N=N, seed=seed)
     bf16 = dtype == "bf16"
-    tdt = torch.bfloat16 if bf16 else torch.float32
+    tdt = TORCH_DTYPE[dtype]
     x = to_dev(inp["x"], dtype)
     dy = to_dev(inp["dy"], dtype)
     w = to_dev(inp["w"], dtype) if with_w else None
@@ -100,9 +102,9 @@ def test_small_shapes(orc, kind, dtype, M, N):
 
 
 @pytest.mark.parametrize("kind", ["ln", "rms"])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_widest_rows(orc, kind, dtype):
-    N = 65536 if dtype == "bf16" else 32768
+    N = 32768 if dtype == "f32" else 65536
     print(f"case {kind} {dtype} 3x{N}", flush=True)
     run_case(orc, kind, dtype, 3, N)
 
@@ -142,6 +144,16 @@ def test_full_size_workloads(orc, name):
     print(f"case {name}", flush=True)
     report = []
     run_case(orc, wl.kind, wl.dtype, M, N, guard=True, report=report)
+    for r in report:
+        print(r, flush=True)
+
+
+@pytest.mark.parametrize("kind,shape", [("rms", (16384, 4096)), ("ln", (25216, 768))])
+def test_full_size_f16(orc, kind, shape):
+    """The two large row-wise workloads with fp16 I/O (same recipe)."""
+    print(f"case {kind} f16 {shape}", flush=True)
+    report = []
+    run_case(orc, kind, "f16", *shape, guard=True, report=report)
     for r in report:
         print(r, flush=True)
 
