@@ -14,7 +14,16 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build", "mi355norm")
 OUT = os.path.join(HERE, "libmi355norm.so")
-SOURCES = ["api_common.hip", "rownorm.hip", "batchnorm.hip"]
+# (source, object name, extra flags): row_inst.hip and bn_inst.hip are
+# compiled once per I/O dtype (and row operation) so the kernels build in
+# parallel.
+SOURCES = [("api_common.hip", "api_common", []), ("rownorm.hip", "rownorm", []),
+           ("batchnorm.hip", "batchnorm", []),
+           *[("row_inst.hip", f"row_{io}_{op}", [f"-DMI355NORM_ROW_IO={i}", f"-DMI355NORM_ROW_RMS={r}"])
+             for i, io in enumerate(("f32", "bf16", "f16")) for r, op in enumerate(("ln", "rms"))],
+           ("bn_inst.hip", "bn_f32", ["-DMI355NORM_BN_IO=0"]),
+           ("bn_inst.hip", "bn_bf16", ["-DMI355NORM_BN_IO=1"]),
+           ("bn_inst.hip", "bn_f16", ["-DMI355NORM_BN_IO=2"])]
 ARCH = os.environ.get("MI355NORM_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -28,13 +37,13 @@ def build(verbose: bool = False) -> str:
     t0 = time.time()
     procs = []
     objs = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+    for src, name, extra in SOURCES:
+        obj = os.path.join(BUILD, name + ".o")
         objs.append(obj)
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        procs.append((name, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     failed = []
     for src, p in procs:
         out, _ = p.communicate()

@@ -1,0 +1,537 @@
+// bn_cols.hpp -- BatchNorm column path: kernels and launchers for inputs
+// whose (n, c) planes are too short to stream on their own -- BatchNorm1d's
+// (N, C) inputs (HW = 1) and (N, C, L) inputs with small L, and small
+// feature maps.
+//
+// Pages (by title):
+//   [NormPage] "How attorch implements LayerNorm, BatchNorm and RMSNorm:
+//               the three normalization Triton kernels explained"
+//   [MathPage] "Building custom GPU operators quickly with attorch.math:
+//               an operator-fusion guide for advanced developers"
+//
+// Layout.  Each sample n is one contiguous row of K = C * HW values; column
+// j holds channel j / HW.  The channel's statistics run down the columns,
+// so a wave reads whole 128-bit vectors along a row and walks down the rows
+// (BnColGeom): every load is a full contiguous segment, whatever HW is.
+//
+//   forward (training)
+//     bn_col_stats_kernel     Welford update per column over the thread's
+//                             rows (float32), merged across the workgroup's
+//                             row slices in float64 (Chan's pairwise merge,
+//                             a fixed tree); one (mean, M2) per column and
+//                             row tile
+//     bn_col_finalize_kernel  one wave per channel combines its HW columns x
+//                             T tiles with the exact parallel-axis identity
+//                             (float64), saves mean / rstd and applies the
+//                             momentum update
+//     bn_col_apply_kernel     z = x * a_c + s_c (+ res), y = act(z)
+//   forward (eval)            bn_col_apply_kernel from the running stats
+//   backward
+//     bn_col_bwd_reduce_kernel   dz = dy * act'(z) at the recomputed z,
+//                             dres = dz, and per column and tile the sums
+//                             of dz, dz (x - mean) and x - mean
+//     bn_col_bwd_finalize_kernel one wave per channel adds them, writes dw,
+//                             db and the dx coefficients (bn_dx_coeffs)
+//     bn_col_bwd_dx_kernel    dx = k1 dz + k2 (x - mean) + k3
+// The per-element arithmetic is the plane path's (same coefficient and
+// activation functions), so both paths compute the same z.
+#pragma once
+
+#include "bn_common.hpp"
+
+namespace mi355norm {
+
+// Position of this thread in the column geometry.
+struct ColPos {
+    int64_t col0;    // first of the thread's V columns
+    int64_t r0, r1;  // the tile's rows [r0, r1)
+    int rs;          // row slice: rows r0 + rs, r0 + rs + RPP, ...
+    int tile;
+    bool active;     // lane maps to a real vector of a real slice
+};
+
+__device__ __forceinline__ ColPos col_pos(const BnColGeom &g, int V) {
+    ColPos p;
+    const int chunk = (int)(blockIdx.x % (unsigned)g.NCH);
+    p.tile = (int)(blockIdx.x / (unsigned)g.NCH);
+    const int cv = (int)(threadIdx.x % (unsigned)g.CV);
+    p.rs = (int)(threadIdx.x / (unsigned)g.CV);
+    const int64_t vi = (int64_t)chunk * g.CV + cv;
+    p.active = p.rs < g.RPP && vi < g.KV;
+    p.col0 = vi * V;
+    p.r0 = (int64_t)p.tile * g.RT;
+    const int64_t e = p.r0 + g.RT;
+    p.r1 = e < g.Nb ? e : g.Nb;
+    return p;
+}
+
+__device__ __forceinline__ int tree_start(int rpp) {
+    int h = 1;
+    while (h < rpp) h <<= 1;
+    return h >> 1;
+}
+
+// -------------------------------------------------------- forward: stats
+template <typename T, int V>
+__global__ void __launch_bounds__(kBnBlock)
+bn_col_stats_kernel(const T *__restrict__ x, BnColGeom g, double *__restrict__ part) {
+    using VT = Vec<T, V>;
+    using raw_t = typename VT::raw_t;
+    const ColPos p = col_pos(g, V);
+    float n = 0.0f, mean[V], m2[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) mean[e] = m2[e] = 0.0f;
+    if (p.active) {
+        const T *base = x + p.col0;
+        const int64_t step = (int64_t)g.RPP;
+        for (int64_t r = p.r0 + p.rs; r < p.r1; r += step * kBnUnroll) {
+            raw_t buf[kBnUnroll];
+#pragma unroll
+            for (int u = 0; u < kBnUnroll; ++u) {
+                const int64_t rr = r + u * step;
+                if (rr < p.r1) buf[u] = vload_stream<T, V>(base + rr * g.K);
+            }
+#pragma unroll
+            for (int u = 0; u < kBnUnroll; ++u) {
+                const int64_t rr = r + u * step;
+                if (rr < p.r1) {
+                    float f[V];
+                    VT::unpack(buf[u], f);
+                    n += 1.0f;
+                    const float inv = 1.0f / n;
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        const float d = f[e] - mean[e];
+                        mean[e] = fmaf(d, inv, mean[e]);
+                        m2[e] = fmaf(d, f[e] - mean[e], m2[e]);
+                    }
+                }
+            }
+        }
+    }
+    // Merge the row slices of each column: a fixed float64 tree over rs.
+    __shared__ double sh_n[kBnBlock];
+    __shared__ double sh_mean[kBnBlock * V];
+    __shared__ double sh_m2[kBnBlock * V];
+    const int t = threadIdx.x;
+    sh_n[t] = n;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        sh_mean[t * V + e] = mean[e];
+        sh_m2[t * V + e] = m2[e];
+    }
+    for (int h = tree_start(g.RPP); h >= 1; h >>= 1) {
+        __syncthreads();
+        if (p.active && p.rs < h && p.rs + h < g.RPP) {
+            const int o = t + h * g.CV;
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const WelfD m = welf_merge(WelfD{sh_n[t], sh_mean[t * V + e], sh_m2[t * V + e]},
+                                           WelfD{sh_n[o], sh_mean[o * V + e], sh_m2[o * V + e]});
+                sh_mean[t * V + e] = m.mean;
+                sh_m2[t * V + e] = m.m2;
+            }
+            sh_n[t] += sh_n[o];
+        }
+    }
+    __syncthreads();
+    if (p.active && p.rs == 0) {
+        double *dst = part + ((int64_t)p.tile * g.K + p.col0) * 2;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            dst[2 * e] = sh_mean[t * V + e];
+            dst[2 * e + 1] = sh_m2[t * V + e];
+        }
+    }
+}
+
+// ------------------------------------------- forward: channel statistics
+// One wave per channel.  Entry (tile, column) holds the n_t rows of the
+// tile as (mean, M2).  Each lane folds its entries (four loads in flight)
+// with Chan's pairwise merge in float64, then the lanes are merged by a
+// butterfly (the merge is symmetric, so every lane ends with the same
+// bits); one pass over the entries, in a fixed order.  (T is only the
+// dtype of the operation, so each dtype's translation unit has its own
+// instance.)
+template <typename T>
+__global__ void __launch_bounds__(kBnBlock)
+bn_col_finalize_kernel(const double *__restrict__ part, BnColGeom g, float eps, float momentum,
+                       float *__restrict__ running_mean, float *__restrict__ running_var,
+                       float *__restrict__ save_mean, float *__restrict__ save_rstd) {
+    constexpr int U = 4;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t c = (int64_t)blockIdx.x * kBnWaves + threadIdx.x / kWave;
+    if (c >= g.C) return;  // the whole wave leaves; no barrier follows
+    const int64_t ne = (int64_t)g.T * g.HW;
+    WelfD acc{0.0, 0.0, 0.0};
+    for (int64_t e0 = lane; e0 < ne; e0 += (int64_t)kWave * U) {
+        double nt[U], m[U], q[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e = e0 + (int64_t)u * kWave;
+            nt[u] = m[u] = q[u] = 0.0;
+            if (e < ne) {
+                const int64_t t = e / g.HW, j = c * g.HW + e % g.HW;
+                const int64_t left = g.Nb - t * g.RT;
+                nt[u] = (double)(left < g.RT ? left : g.RT);
+                m[u] = part[(t * g.K + j) * 2];
+                q[u] = part[(t * g.K + j) * 2 + 1];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc = welf_merge(acc, WelfD{nt[u], m[u], q[u]});
+    }
+#pragma unroll
+    for (int s = kWave / 2; s >= 1; s >>= 1)
+        acc = welf_merge(acc, WelfD{shfl_xor_d(acc.n, s), shfl_xor_d(acc.mean, s), shfl_xor_d(acc.m2, s)});
+    if (lane == 0) bn_save_stats(acc, c, eps, momentum, running_mean, running_var, save_mean, save_rstd);
+}
+
+// ---------------------------------------------------- forward: apply
+// MODE 0 (training): mean / rstd from save_mean / save_rstd (just written
+// by the finalize kernel).  MODE 1 (eval): from the running statistics.
+template <typename T, int V, int ACT, bool RES, int MODE>
+__global__ void __launch_bounds__(kBnBlock)
+bn_col_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__restrict__ w,
+                    const T *__restrict__ b, const float *__restrict__ mean_src,
+                    const float *__restrict__ scale_src, float eps, T *__restrict__ y, BnColGeom g,
+                    int act_rt, float act_p) {
+    using VT = Vec<T, V>;
+    using raw_t = typename VT::raw_t;
+    constexpr bool kFast = std::is_same<T, bf16_t>::value;  // fp16 keeps the exact forms
+    const ColPos p = col_pos(g, V);
+    if (!p.active) return;  // no barriers in this kernel
+    float a[V], s[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        const int64_t c = (p.col0 + e) / g.HW;
+        const float mean = mean_src[c];
+        const float rstd = MODE == 0 ? scale_src[c] : 1.0f / sqrtf(scale_src[c] + eps);
+        bn_coeffs(mean, rstd, w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a[e], &s[e]);
+    }
+    const int64_t step = (int64_t)g.RPP;
+    for (int64_t r = p.r0 + p.rs; r < p.r1; r += step * kBnUnroll) {
+        raw_t rx[kBnUnroll], rr_[kBnUnroll];
+#pragma unroll
+        for (int u = 0; u < kBnUnroll; ++u) {
+            const int64_t row = r + u * step;
+            if (row < p.r1) {
+                rx[u] = vload_stream<T, V>(x + row * g.K + p.col0);
+                if (RES) rr_[u] = vload_stream<T, V>(res + row * g.K + p.col0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kBnUnroll; ++u) {
+            const int64_t row = r + u * step;
+            if (row < p.r1) {
+                float f[V], rf[V], o[V];
+                VT::unpack(rx[u], f);
+                if (RES) VT::unpack(rr_[u], rf);
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    float z = fmaf(f[e], a[e], s[e]);
+                    if (RES) z += rf[e];
+                    o[e] = act_fwd_any<ACT, kFast>(z, act_rt, act_p);
+                }
+                vstore_stream<T, V>(y + row * g.K + p.col0, VT::pack(o));
+            }
+        }
+    }
+}
+
+// --------------------------------------------------- backward: pass 1
+// Accumulation as on the plane path: float64 per element for float32 I/O
+// (with the sum of x - mean), float32 dz and dz * x per thread for 16-bit
+// I/O (the mean taken out per tile in float64); the row slices are added
+// in float64 by a fixed tree.
+template <typename T, int V, int ACT, bool RES>
+__global__ void __launch_bounds__(kBnBlock)
+bn_col_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__restrict__ res,
+                         const T *__restrict__ w, const T *__restrict__ b,
+                         const float *__restrict__ save_mean, const float *__restrict__ save_rstd,
+                         T *__restrict__ dres, BnColGeom g, double *__restrict__ part, int act_rt,
+                         float act_p) {
+    using VT = Vec<T, V>;
+    using raw_t = typename VT::raw_t;
+    constexpr bool kExact = sizeof(T) == 4;
+    constexpr bool kFast = kFastGrad<T>;
+    constexpr int NS = kExact ? 3 : 2;
+    using Acc = typename std::conditional<kExact, double, float>::type;
+    const ColPos p = col_pos(g, V);
+    Acc s_dz[V], s_dzx[V], s_xc[V];
+    float a[V], s[V], mean[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        s_dz[e] = s_dzx[e] = s_xc[e] = 0;
+        a[e] = s[e] = mean[e] = 0.0f;
+    }
+    if (p.active) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const int64_t c = (p.col0 + e) / g.HW;
+            mean[e] = save_mean[c];
+            bn_coeffs(mean[e], save_rstd[c], w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a[e], &s[e]);
+        }
+        const int64_t step = (int64_t)g.RPP;
+        for (int64_t r = p.r0 + p.rs; r < p.r1; r += step * kBnUnroll) {
+            raw_t rd[kBnUnroll], rx[kBnUnroll], rr_[kBnUnroll];
+#pragma unroll
+            for (int u = 0; u < kBnUnroll; ++u) {
+                const int64_t row = r + u * step;
+                if (row < p.r1) {
+                    const int64_t off = row * g.K + p.col0;
+                    rd[u] = vload_stream<T, V>(dy + off);
+                    rx[u] = vload_stream<T, V>(x + off);
+                    if (RES && ACT != kActNone) rr_[u] = vload_stream<T, V>(res + off);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kBnUnroll; ++u) {
+                const int64_t row = r + u * step;
+                if (row < p.r1) {
+                    float df[V], xf[V], rf[V], dz[V];
+                    VT::unpack(rd[u], df);
+                    VT::unpack(rx[u], xf);
+                    if (RES && ACT != kActNone) VT::unpack(rr_[u], rf);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        if (ACT != kActNone) {
+                            float z = fmaf(xf[e], a[e], s[e]);
+                            if (RES) z += rf[e];
+                            dz[e] = df[e] * act_grad_any<ACT, kFast>(z, act_rt, act_p);
+                        } else {
+                            dz[e] = df[e];
+                        }
+                        const Acc xc = kExact ? (Acc)xf[e] - (Acc)mean[e] : (Acc)xf[e];
+                        const Acc d = (Acc)dz[e];
+                        s_dz[e] += d;
+                        s_dzx[e] = fma(d, xc, s_dzx[e]);
+                        if (kExact) s_xc[e] += xc;
+                    }
+                    if (RES) vstore_stream<T, V>(dres + row * g.K + p.col0, VT::pack(dz));
+                }
+            }
+        }
+    }
+    __shared__ double sh[NS][kBnBlock * V];
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        sh[0][t * V + e] = (double)s_dz[e];
+        sh[1][t * V + e] = (double)s_dzx[e];
+        if (kExact) sh[NS - 1][t * V + e] = (double)s_xc[e];
+    }
+    for (int h = tree_start(g.RPP); h >= 1; h >>= 1) {
+        __syncthreads();
+        if (p.active && p.rs < h && p.rs + h < g.RPP) {
+            const int o = t + h * g.CV;
+#pragma unroll
+            for (int k = 0; k < NS; ++k)
+#pragma unroll
+                for (int e = 0; e < V; ++e) sh[k][t * V + e] += sh[k][o * V + e];
+        }
+    }
+    __syncthreads();
+    if (p.active && p.rs == 0) {
+        double *dst = part + ((int64_t)p.tile * g.K + p.col0) * 3;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const double p0 = sh[0][t * V + e];
+            double p1 = sh[1][t * V + e];
+            if (!kExact) p1 -= (double)mean[e] * p0;  // sum dz * x  ->  sum dz * (x - mean)
+            dst[3 * e] = p0;
+            dst[3 * e + 1] = p1;
+            dst[3 * e + 2] = kExact ? sh[NS - 1][t * V + e] : 0.0;
+        }
+    }
+}
+
+// ------------------------------------------- backward: channel sums
+// One wave per channel: adds the (tile, column) sums in a fixed order,
+// writes db and dw, and stores k1, k2, k3, k3m for the dx kernel.
+template <typename T>
+__global__ void __launch_bounds__(kBnBlock)
+bn_col_bwd_finalize_kernel(const double *__restrict__ part, BnColGeom g, const T *__restrict__ w,
+                           const float *__restrict__ save_mean, const float *__restrict__ save_rstd,
+                           T *__restrict__ dw, T *__restrict__ db, float *__restrict__ coef) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t c = (int64_t)blockIdx.x * kBnWaves + threadIdx.x / kWave;
+    if (c >= g.C) return;  // the whole wave leaves; no barrier follows
+    constexpr int U = 4;  // entries in flight per lane
+    const int64_t ne = (int64_t)g.T * g.HW;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0;
+    for (int64_t e0 = lane; e0 < ne; e0 += (int64_t)kWave * U) {
+        double v[U][3];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e = e0 + (int64_t)u * kWave;
+            v[u][0] = v[u][1] = v[u][2] = 0.0;
+            if (e < ne) {
+                const int64_t t = e / g.HW, j = c * g.HW + e % g.HW;
+                const double *q = part + (t * g.K + j) * 3;
+                v[u][0] = q[0];
+                v[u][1] = q[1];
+                v[u][2] = q[2];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            s0 += v[u][0];
+            s1 += v[u][1];
+            s2 += v[u][2];
+        }
+    }
+    double sums[3] = {wave_sum_d(s0), wave_sum_d(s1), wave_sum_d(s2)};
+    if (lane == 0) {
+        const double n_total = (double)g.Nb * (double)g.HW;
+        const BnDxCoef k = bn_dx_coeffs(sums, save_mean[c], save_rstd[c], w ? ld1(w + c) : 1.0f, n_total);
+        if (db) st1(db + c, (float)k.dbeta);
+        if (dw) st1(dw + c, (float)k.dgamma);
+        coef[c * 4 + 0] = k.k1;
+        coef[c * 4 + 1] = k.k2;
+        coef[c * 4 + 2] = k.k3;
+        coef[c * 4 + 3] = k.k3m;
+    }
+}
+
+// ----------------------------------------------------- backward: pass 2
+// DZ_SRC as on the plane path: 0 dz = dy; 1 dz re-read from dres; 2 dz
+// recomputed from dy, x (and res).
+template <typename T, int V, int ACT, bool RES, int DZ_SRC>
+__global__ void __launch_bounds__(kBnBlock)
+bn_col_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__restrict__ res,
+                     const T *__restrict__ dres, const T *__restrict__ w, const T *__restrict__ b,
+                     const float *__restrict__ save_mean, const float *__restrict__ save_rstd,
+                     const float *__restrict__ coef, T *__restrict__ dx, BnColGeom g, int act_rt,
+                     float act_p) {
+    using VT = Vec<T, V>;
+    using raw_t = typename VT::raw_t;
+    constexpr bool kExact = sizeof(T) == 4;
+    constexpr bool kFast = kFastGrad<T>;
+    const ColPos p = col_pos(g, V);
+    if (!p.active) return;  // no barriers in this kernel
+    float k1[V], k2[V], k3[V], mean[V], a[V], s[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        const int64_t c = (p.col0 + e) / g.HW;
+        k1[e] = coef[c * 4 + 0];
+        k2[e] = coef[c * 4 + 1];
+        k3[e] = kExact ? coef[c * 4 + 2] : coef[c * 4 + 3];
+        mean[e] = save_mean[c];
+        a[e] = s[e] = 0.0f;
+        if (DZ_SRC == 2)
+            bn_coeffs(mean[e], save_rstd[c], w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a[e], &s[e]);
+    }
+    const T *dzsrc = DZ_SRC == 1 ? dres : dy;
+    const int64_t step = (int64_t)g.RPP;
+    for (int64_t r = p.r0 + p.rs; r < p.r1; r += step * kBnUnroll) {
+        raw_t rd[kBnUnroll], rx[kBnUnroll], rr_[kBnUnroll];
+#pragma unroll
+        for (int u = 0; u < kBnUnroll; ++u) {
+            const int64_t row = r + u * step;
+            if (row < p.r1) {
+                const int64_t off = row * g.K + p.col0;
+                rd[u] = vload_stream<T, V>(dzsrc + off);
+                rx[u] = vload_stream<T, V>(x + off);
+                if (DZ_SRC == 2 && RES) rr_[u] = vload_stream<T, V>(res + off);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kBnUnroll; ++u) {
+            const int64_t row = r + u * step;
+            if (row < p.r1) {
+                float df[V], xf[V], rf[V], o[V];
+                VT::unpack(rd[u], df);
+                VT::unpack(rx[u], xf);
+                if (DZ_SRC == 2 && RES) VT::unpack(rr_[u], rf);
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    float dz = df[e];
+                    if (DZ_SRC == 2 && ACT != kActNone) {
+                        float z = fmaf(xf[e], a[e], s[e]);
+                        if (RES) z += rf[e];
+                        dz = df[e] * act_grad_any<ACT, kFast>(z, act_rt, act_p);
+                    }
+                    o[e] = kExact ? fmaf(k1[e], dz, fmaf(k2[e], xf[e] - mean[e], k3[e]))
+                                  : fmaf(k1[e], dz, fmaf(k2[e], xf[e], k3[e]));
+                }
+                vstore_stream<T, V>(dx + row * g.K + p.col0, VT::pack(o));
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- launchers
+
+template <typename T, int V, int MODE>
+static auto col_apply_kernel(norm_act act, bool r) {
+    switch (act) {
+    case NORM_ACT_NONE: return r ? bn_col_apply_kernel<T, V, kActNone, true, MODE> : bn_col_apply_kernel<T, V, kActNone, false, MODE>;
+    case NORM_ACT_RELU: return r ? bn_col_apply_kernel<T, V, kActRelu, true, MODE> : bn_col_apply_kernel<T, V, kActRelu, false, MODE>;
+    case NORM_ACT_GELU: return r ? bn_col_apply_kernel<T, V, kActGelu, true, MODE> : bn_col_apply_kernel<T, V, kActGelu, false, MODE>;
+    default: return r ? bn_col_apply_kernel<T, V, kActGeneric, true, MODE> : bn_col_apply_kernel<T, V, kActGeneric, false, MODE>;
+    }
+}
+
+template <typename T, int V>
+norm_status bn_col_fwd_train(const BnColGeom &g, const BnArgs &a) {
+    const dim3 grid((unsigned)((int64_t)g.NCH * g.T));
+    const dim3 fgrid((unsigned)ceil_div(g.C, kBnWaves));
+    double *part = static_cast<double *>(a.ws);
+    launch("bn_col_stats_kernel", false, bn_col_stats_kernel<T, V>, grid, dim3(kBnBlock), 0, a.st,
+           (const T *)a.x, g, part);
+    launch("bn_col_finalize_kernel", false, bn_col_finalize_kernel<T>, fgrid, dim3(kBnBlock), 0, a.st,
+           (const double *)part, g, a.eps, a.momentum, a.rm, a.rv, a.sm, a.sr);
+    launch("bn_col_apply_kernel<train>", true, col_apply_kernel<T, V, 0>(a.act, a.res != nullptr), grid,
+           dim3(kBnBlock), 0, a.st, (const T *)a.x, (const T *)a.res, (const T *)a.w, (const T *)a.b,
+           (const float *)a.sm, (const float *)a.sr, a.eps, (T *)a.y, g, (int)a.act, a.act_p);
+    return launch_status();
+}
+
+template <typename T, int V>
+norm_status bn_col_fwd_eval(const BnColGeom &g, const BnArgs &a) {
+    const dim3 grid((unsigned)((int64_t)g.NCH * g.T));
+    launch("bn_col_apply_kernel<eval>", true, col_apply_kernel<T, V, 1>(a.act, a.res != nullptr), grid,
+           dim3(kBnBlock), 0, a.st, (const T *)a.x, (const T *)a.res, (const T *)a.w, (const T *)a.b,
+           (const float *)a.rm, (const float *)a.rv, a.eps, (T *)a.y, g, (int)a.act, a.act_p);
+    return launch_status();
+}
+
+template <typename T, int V, int ACT>
+static void col_bwd_act(const BnColGeom &g, const BnArgs &a) {
+    const dim3 grid((unsigned)((int64_t)g.NCH * g.T));
+    const dim3 fgrid((unsigned)ceil_div(g.C, kBnWaves));
+    const dim3 blk(kBnBlock);
+    double *part = static_cast<double *>(a.ws);
+    float *coef = reinterpret_cast<float *>(static_cast<char *>(a.ws) + col_part_bytes_host(g));
+    const bool has_res = a.res != nullptr;
+    const int act_rt = (int)a.act;
+    launch("bn_col_bwd_reduce_kernel", has_res,
+           has_res ? bn_col_bwd_reduce_kernel<T, V, ACT, true> : bn_col_bwd_reduce_kernel<T, V, ACT, false>, grid,
+           blk, 0, a.st, (const T *)a.dy, (const T *)a.x, (const T *)a.res, (const T *)a.w, (const T *)a.b,
+           (const float *)a.sm, (const float *)a.sr, (T *)a.dres, g, part, act_rt, a.act_p);
+    launch("bn_col_bwd_finalize_kernel", false, bn_col_bwd_finalize_kernel<T>, fgrid, blk, 0, a.st,
+           (const double *)part, g, (const T *)a.w, (const float *)a.sm, (const float *)a.sr, (T *)a.dw,
+           (T *)a.db, coef);
+    const bool fp32 = sizeof(T) == 4;
+    auto fn = bn_col_bwd_dx_kernel<T, V, ACT, false, 2>;
+    if (ACT == kActNone && !has_res) fn = bn_col_bwd_dx_kernel<T, V, ACT, false, 0>;
+    else if (has_res && (fp32 || ACT == kActNone)) fn = bn_col_bwd_dx_kernel<T, V, ACT, true, 1>;
+    else if (has_res) fn = bn_col_bwd_dx_kernel<T, V, ACT, true, 2>;
+    launch("bn_col_bwd_dx_kernel", !has_res, fn, grid, blk, 0, a.st, (const T *)a.dy, (const T *)a.x,
+           (const T *)a.res, (const T *)a.dres, (const T *)a.w, (const T *)a.b, (const float *)a.sm,
+           (const float *)a.sr, (const float *)coef, (T *)a.dx, g, act_rt, a.act_p);
+}
+
+template <typename T, int V>
+norm_status bn_col_bwd(const BnColGeom &g, const BnArgs &a) {
+    switch (a.act) {
+    case NORM_ACT_NONE: col_bwd_act<T, V, kActNone>(g, a); break;
+    case NORM_ACT_RELU: col_bwd_act<T, V, kActRelu>(g, a); break;
+    case NORM_ACT_GELU: col_bwd_act<T, V, kActGelu>(g, a); break;
+    default: col_bwd_act<T, V, kActGeneric>(g, a); break;
+    }
+    return launch_status();
+}
+
+}  // namespace mi355norm

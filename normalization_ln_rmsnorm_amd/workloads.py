@@ -38,6 +38,11 @@ The six workloads (sizes as the benchmark runs them):
                          sd_c ~ U(0.2,4); no residual; dy ~ N(0,1); w/b as
                          above; momentum 0.1, eps 1e-5; running mean 0 and
                          running variance 1 at the start
+
+EXTRA_WORKLOADS adds fp16 variants of the RMSNorm and bf16 BatchNorm
+workloads and two BatchNorm1d workloads (same recipe as the BatchNorm2d
+ones): (N, C) = 8192 x 2048 fp32 with ReLU, and (N, C, L) = 2048 x 512 x 32
+bf16 with residual + GELU and an eval step.
 """
 from dataclasses import dataclass, field
 
@@ -96,12 +101,20 @@ def _variant(base: str, name: str, **changes) -> Workload:
 
 
 # Variants beyond the six above, measured alongside them: the same recipes
-# with fp16 I/O.
+# with fp16 I/O, and BatchNorm1d inputs -- (N, C) with HW = 1 and (N, C, L)
+# -- whose planes are too short for the plane path.  Shapes stored as
+# (N, C, L, 1).
 EXTRA_WORKLOADS = {
     w.name: w
     for w in [
         _variant("rms_bf16_16384x4096", "rms_f16_16384x4096", dtype="f16"),
         _variant("bn_bf16_256x64x112x112", "bn_f16_256x64x112x112", dtype="f16"),
+        Workload("bn1d_f32_8192x2048", "bn", "f32", (8192, 2048, 1, 1), 1005, 1e-5,
+                 momentum=0.1, act="relu", residual=False,
+                 extra=dict(mu_range=(-2.0, 2.0), sd_range=(0.5, 3.0))),
+        Workload("bn1d_bf16_2048x512x32", "bn", "bf16", (2048, 512, 32, 1), 1006, 1e-5,
+                 momentum=0.1, act="gelu", residual=True, eval_after_train=True,
+                 extra=dict(mu_range=(-1.0, 1.0), sd_range=(0.2, 4.0))),
     ]
 }
 

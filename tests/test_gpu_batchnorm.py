@@ -16,7 +16,7 @@ from tests._parity import avoid_kinks, check, to_dev, to_f64, to_io
 pytestmark = pytest.mark.gpu
 
 nl = pytest.importorskip("normalization_ln_rmsnorm_amd")
-from normalization_ln_rmsnorm_amd.workloads import WORKLOADS, gen_bn  # noqa: E402
+from normalization_ln_rmsnorm_amd.workloads import EXTRA_WORKLOADS, WORKLOADS, gen_bn  # noqa: E402
 
 
 def _wl(dtype, act, residual):
@@ -147,6 +147,43 @@ def test_full_size_workloads(orc, name):
     report = []
     run_case(orc, wl.dtype, Nb, C, H * W, wl.act, wl.residual, eval_after=True, report=report,
              wl=wl)
+    for r in report:
+        print(r, flush=True)
+
+
+# BatchNorm1d shapes: (N, C) with HW = 1 and (N, C, L); they take the
+# column path (vector or scalar, depending on whether C * HW splits into
+# 128-bit vectors).
+BN1D = [(4096, 64, 1), (3, 5, 1), (1000, 333, 1), (256, 1024, 1), (64, 32, 16), (33, 7, 49),
+        (16, 128, 49), (2, 3, 2), (517, 24, 3)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("act,residual", [("relu", True), ("gelu", False), ("silu", True)])
+@pytest.mark.parametrize("Nb,C,HW", BN1D)
+def test_bn1d_shapes(orc, dtype, act, residual, Nb, C, HW):
+    print(f"case bn1d {dtype} {Nb}x{C}x{HW} {act} res={residual}", flush=True)
+    run_case(orc, dtype, Nb, C, HW, act, residual)
+
+
+@pytest.mark.parametrize("path", ["plane", "cols"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Nb,C,HW", [(4, 8, 49), (7, 3, 1000), (8, 16, 64), (300, 40, 1)])
+def test_each_path_on_every_shape(orc, monkeypatch, path, dtype, Nb, C, HW):
+    """Either data path, forced, meets the tolerance on shapes that would
+    normally take the other."""
+    monkeypatch.setenv("MI355NORM_BN_PATH", path)
+    print(f"case bn path={path} {dtype} {Nb}x{C}x{HW}", flush=True)
+    run_case(orc, dtype, Nb, C, HW, "gelu", True)
+
+
+@pytest.mark.parametrize("name", ["bn1d_f32_8192x2048", "bn1d_bf16_2048x512x32"])
+def test_full_size_bn1d(orc, name):
+    wl = EXTRA_WORKLOADS[name]
+    Nb, C, L, _ = wl.shape
+    print(f"case {name}", flush=True)
+    report = []
+    run_case(orc, wl.dtype, Nb, C, L, wl.act, wl.residual, report=report, wl=wl)
     for r in report:
         print(r, flush=True)
 
