@@ -25,6 +25,8 @@ ACT = {"none": 0, "relu": 1, "gelu": 2, "sigmoid": 3, "tanh": 4, "silu": 5, "mis
 
 _D = ctypes.POINTER(ctypes.c_double)
 _I64 = ctypes.c_int64
+_U32P = ctypes.POINTER(ctypes.c_uint32)
+_U8P = ctypes.POINTER(ctypes.c_uint8)
 
 
 def _load():
@@ -49,6 +51,12 @@ def _load():
         "orc_bn_bwd": [_I64, _I64, _I64, ctypes.c_double, ctypes.c_int, ctypes.c_double,
                        _D, _D, _D, _D, _D, _D, _D, _D, _D],
         "orc_welford": [_I64, _D, _D],
+        "orc_philox4x32_10": [_U32P, _U32P, _U32P],
+        "orc_dropout_keep": [_I64, ctypes.c_double, ctypes.c_uint64, ctypes.c_uint64, _U8P],
+        "orc_act_dropout_fwd": [_I64, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                ctypes.c_uint64, ctypes.c_uint64, _D, _D],
+        "orc_act_dropout_bwd": [_I64, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                ctypes.c_uint64, ctypes.c_uint64, _D, _D, _D],
         "orc_chan_merge": [_D, _D, _D],
     }
     for name, argtypes in sigs.items():
@@ -56,6 +64,8 @@ def _load():
         fn.argtypes = argtypes
         fn.restype = None
     lib.orc_num_threads.restype = ctypes.c_int
+    lib.orc_dropout_threshold.argtypes = [ctypes.c_double]
+    lib.orc_dropout_threshold.restype = ctypes.c_uint32
     _lib = lib
     return lib
 
@@ -187,6 +197,47 @@ def bn_bwd(dy, x, res=None, w=None, b=None, eps=1e-5, act="none", bf16=False, ac
     _load().orc_bn_bwd(Nb, C, HW, eps, ACT[act], float(act_param), _p(dy), _p(x), _p(res), _p(w), _p(b),
                        _p(dx), _p(dres), _p(dw), _p(db))
     return dx, dres, dw, db
+
+
+# ------------------------------------------------- activation + dropout
+def philox4x32_10(ctr, key):
+    """The four output words of Philox4x32-10 for a 4-word counter and a
+    2-word key."""
+    c = (ctypes.c_uint32 * 4)(*[int(v) & 0xFFFFFFFF for v in ctr])
+    k = (ctypes.c_uint32 * 2)(*[int(v) & 0xFFFFFFFF for v in key])
+    o = (ctypes.c_uint32 * 4)()
+    _load().orc_philox4x32_10(c, k, o)
+    return [int(v) for v in o]
+
+
+def dropout_threshold(p):
+    return int(_load().orc_dropout_threshold(float(p)))
+
+
+def dropout_keep(n, p, seed, offset=0):
+    """uint8 keep mask of elements offset .. offset + n - 1."""
+    keep = np.empty(int(n), dtype=np.uint8)
+    _load().orc_dropout_keep(int(n), float(p), int(seed), int(offset),
+                             keep.ctypes.data_as(_U8P))
+    return keep
+
+
+def act_dropout_fwd(x, act="none", p=0.0, seed=0, offset=0, act_param=0.0, bf16=False):
+    """y = keep ? act(x) / (1 - p) : 0 over the flattened x (float64)."""
+    x = _f(x, bf16)
+    y = np.empty_like(x)
+    _load().orc_act_dropout_fwd(x.size, ACT[act], float(act_param), float(p), int(seed), int(offset),
+                                _p(x), _p(y))
+    return y
+
+
+def act_dropout_bwd(dy, x, act="none", p=0.0, seed=0, offset=0, act_param=0.0, bf16=False):
+    """dx = keep ? dy * act'(x) / (1 - p) : 0 (float64)."""
+    dy = _f(dy, bf16); x = _f(x, bf16)
+    dx = np.empty_like(x)
+    _load().orc_act_dropout_bwd(x.size, ACT[act], float(act_param), float(p), int(seed), int(offset),
+                                _p(dy), _p(x), _p(dx))
+    return dx
 
 
 # ------------------------------------------------------ one-pass statistics

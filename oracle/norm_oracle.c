@@ -426,3 +426,63 @@ void orc_chan_merge(const double a[3], const double b[3], double out[3]) {
     out[1] = mean;
     out[2] = m2;
 }
+
+/* ---------------------------------------------------- activation + dropout
+ * Philox4x32-10 as published by Salmon et al. (SC 2011): ten rounds of
+ *   (c0, c1, c2, c3) <- (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0))
+ * with M0 = 0xD2511F53, M1 = 0xCD9E8D57, the key bumped by the Weyl
+ * constants (0x9E3779B9, 0xBB67AE85) between rounds. */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+uint32_t orc_dropout_threshold(double p) {
+    if (!(p > 0.0)) return 0;
+    if (p >= 1.0) return 1u << 24;
+    return (uint32_t)floor(p * 16777216.0 + 0.5);
+}
+
+static int orc_kept(uint64_t e, uint64_t seed, uint32_t thresh) {
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    const uint64_t blk = e >> 2;
+    const uint32_t ctr[4] = {(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u};
+    uint32_t w[4];
+    orc_philox4x32_10(ctr, key, w);
+    return (w[e & 3] >> 8) >= thresh;
+}
+
+void orc_dropout_keep(int64_t n, double p, uint64_t seed, uint64_t offset, uint8_t *keep) {
+    const uint32_t t = orc_dropout_threshold(p);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) keep[i] = (uint8_t)orc_kept(offset + (uint64_t)i, seed, t);
+}
+
+void orc_act_dropout_fwd(int64_t n, int act, double act_p, double p, uint64_t seed,
+                         uint64_t offset, const double *x, double *y) {
+    const uint32_t t = orc_dropout_threshold(p);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = orc_kept(offset + (uint64_t)i, seed, t) ? orc_act(act, act_p, x[i]) / (1.0 - p) : 0.0;
+}
+
+void orc_act_dropout_bwd(int64_t n, int act, double act_p, double p, uint64_t seed,
+                         uint64_t offset, const double *dy, const double *x, double *dx) {
+    const uint32_t t = orc_dropout_threshold(p);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        dx[i] = orc_kept(offset + (uint64_t)i, seed, t)
+                    ? dy[i] * orc_act_grad(act, act_p, x[i]) / (1.0 - p) : 0.0;
+}

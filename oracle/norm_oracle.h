@@ -81,6 +81,29 @@ void orc_bn_bwd(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
 /* The one-pass statistics the BatchNorm page describes, used only to show
  * that they reach the two-pass result: Welford's per-value update, and the
  * pairwise merge of two partial (count, mean, M2) triples. */
+/* Activation + dropout ([ActPage] sections 3-5: inverted dropout fused
+ * after the activation; the mask is a function of (seed, element offset)
+ * from a counter-based generator and is recomputed in the backward).
+ *
+ * Generator: Philox4x32-10 (Salmon, Moraes, Dror & Shaw, "Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011).  Element e (the caller's offset
+ * plus its index) takes word e mod 4 of Philox4x32-10 with
+ *   key     = (seed mod 2^32, seed / 2^32)
+ *   counter = ((e / 4) mod 2^32, (e / 4) / 2^32, 0, 0).
+ * The element is dropped when (word >> 8) < T with T = round(p * 2^24)
+ * (ties away from zero), i.e. with probability T / 2^24; a kept element is
+ * scaled by 1 / (1 - p). */
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+uint32_t orc_dropout_threshold(double p);
+/* keep[i] = 1 if element offset + i is kept, else 0. */
+void orc_dropout_keep(int64_t n, double p, uint64_t seed, uint64_t offset, uint8_t *keep);
+/* y = keep ? act(x) / (1 - p) : 0. */
+void orc_act_dropout_fwd(int64_t n, int act, double act_p, double p, uint64_t seed,
+                         uint64_t offset, const double *x, double *y);
+/* dx = keep ? dy * act'(x) / (1 - p) : 0. */
+void orc_act_dropout_bwd(int64_t n, int act, double act_p, double p, uint64_t seed,
+                         uint64_t offset, const double *dy, const double *x, double *dx);
+
 void orc_welford(int64_t n, const double *x, double out[3]);
 void orc_chan_merge(const double a[3], const double b[3], double out[3]);
 
