@@ -109,6 +109,11 @@ def bytes_bn(wl, es):
     return dict(fwd=fwd, bwd=bwd, eval=ev, fwd_kernel=fwd_kernel, bwd_kernel=bwd_kernel)
 
 
+def bytes_act_dropout(wl, es):
+    U = wl.shape[0] * wl.shape[1] * es
+    return dict(fwd=2 * U, bwd=3 * U, fwd_kernel=2 * U, bwd_kernel=3 * U)
+
+
 # ------------------------------------------------------------ workloads
 ELEM_SIZE = {"f32": 4, "bf16": 2, "f16": 2}
 
@@ -210,6 +215,36 @@ class BnBench:
         else:
             nl.bn_fwd_eval(self.x, self.w, self.b, self.rm, self.rv, wl.eps, wl.act, self.res,
                            y=self.ye)
+
+
+class AdBench:
+    """Activation + dropout: forward reads x, writes y; backward reads dy and
+    x, writes dx (the mask recomputed from the seed)."""
+
+    def __init__(self, wl, nl, torch):
+        from normalization_ln_rmsnorm_amd.workloads import gen_act_dropout
+        self.wl, self.nl, self.torch = wl, nl, torch
+        inp = gen_act_dropout(wl)
+        self.x = to_device(torch, inp["x"], wl.dtype)
+        self.dy = to_device(torch, inp["dy"], wl.dtype)
+        del inp
+        self.y = torch.empty_like(self.x)
+        self.dx = torch.empty_like(self.x)
+        self.p, self.seed = wl.extra["drop_p"], wl.extra["dropout_seed"]
+        self.bytes = bytes_act_dropout(wl, ELEM_SIZE[wl.dtype])
+        self.ops = ["fwd", "bwd"]
+        self.dominant = "bwd"
+
+    def run(self, op):
+        nl, wl = self.nl, self.wl
+        if op == "fwd":
+            nl.act_dropout_fwd(self.x, wl.act, self.p, self.seed, 0, y=self.y)
+        else:
+            nl.act_dropout_bwd(self.dy, self.x, wl.act, self.p, self.seed, 0, dx=self.dx)
+
+
+def bench_class(wl):
+    return {"ln": RowBench, "rms": RowBench, "bn": BnBench, "ad": AdBench}[wl.kind]
 
 
 MAX_KERNELS = 4  # kernels per operation timed through the library's hook
@@ -368,8 +403,7 @@ def main():
     name = args.workload or HEADLINE
     every = {**WORKLOADS, **EXTRA_WORKLOADS}
     wl = every[name]
-    mk = RowBench if wl.kind in ("ln", "rms") else BnBench
-    bench = mk(wl, nl, torch)
+    bench = bench_class(wl)(wl, nl, torch)
     meas = measure(bench, args.steps, args.warmup, torch, hip, nl, flush)
     head = summarize(bench, meas)
     wall = meas["wall"]
@@ -382,7 +416,7 @@ def main():
             if other == name:
                 continue
             ow = every[other]
-            b = (RowBench if ow.kind in ("ln", "rms") else BnBench)(ow, nl, torch)
+            b = bench_class(ow)(ow, nl, torch)
             per[other] = summarize(b, measure(b, args.other_steps, 3, torch, hip, nl, flush))
             print(f"[bench] {other}: " + "  ".join(
                 f"{op} {per[other][op]['ms_mean']*1e3:.1f} us {per[other][op]['GBps']:.0f} GB/s"
@@ -414,7 +448,8 @@ def main():
         "metric": METRIC, "value": fb["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": fb["ms"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": name, "op": {"rms": "RMSNorm", "ln": "LayerNorm", "bn": "BatchNorm2d"}[wl.kind] + " fwd+bwd",
+        "config": {"workload": name, "op": {"rms": "RMSNorm", "ln": "LayerNorm", "bn": "BatchNorm",
+                                             "ad": "activation+dropout"}[wl.kind] + " fwd+bwd",
                    "shape": list(wl.shape), "io_dtype": wl.dtype, "eps": wl.eps},
         "pct_of_peak": 100.0 * fb["frac_of_peak"], "rows_per_s": fb["rows_per_s"],
         "fwd": head["fwd"], "bwd": head["bwd"],

@@ -21,6 +21,9 @@ SOURCES = [("api_common.hip", "api_common", []), ("rownorm.hip", "rownorm", []),
            ("batchnorm.hip", "batchnorm", []),
            *[("row_inst.hip", f"row_{io}_{op}", [f"-DMI355NORM_ROW_IO={i}", f"-DMI355NORM_ROW_RMS={r}"])
              for i, io in enumerate(("f32", "bf16", "f16")) for r, op in enumerate(("ln", "rms"))],
+           ("act_dropout.hip", "act_dropout", []),
+           *[("ad_inst.hip", f"ad_{io}", [f"-DMI355NORM_AD_IO={i}"])
+             for i, io in enumerate(("f32", "bf16", "f16"))],
            ("bn_inst.hip", "bn_f32", ["-DMI355NORM_BN_IO=0"]),
            ("bn_inst.hip", "bn_bf16", ["-DMI355NORM_BN_IO=1"]),
            ("bn_inst.hip", "bn_f16", ["-DMI355NORM_BN_IO=2"])]

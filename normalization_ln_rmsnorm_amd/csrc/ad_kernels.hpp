@@ -1,0 +1,212 @@
+// ad_kernels.hpp -- fused activation + dropout, element-wise, for gfx950.
+//
+// Page (by title):
+//   [ActPage] "Operator fusion in practice: attorch's activation and
+//             dropout fusion kernels" -- sections 3-5 (one load and one
+//             store per element, the activation and inverted dropout applied
+//             in registers; the mask a function of (seed, element offset)
+//             recomputed in the backward instead of stored) and 6 (one
+//             kernel per activation, the rest pruned at compile time).
+//
+// Mask.  Element e (the caller's offset, a multiple of 4, plus the flat
+// index) takes word e mod 4 of Philox4x32-10 (Salmon et al., SC 2011) under
+// key (seed low, seed high) and counter (e / 4 low, e / 4 high, 0, 0): one
+// generator call yields the words of four consecutive elements, so a
+// float32 vector costs one call and a 16-bit vector two.  The element is
+// dropped when (word >> 8) < thresh (thresh / 2^24 is the drop
+// probability); survivors are scaled by 1 / (1 - p).
+//
+// Both directions are bound by HBM traffic (2 tensors forward, 3 backward);
+// the ten Philox rounds cost ~20 VALU operations per element, a fraction of
+// the VALU budget at 8 TB/s.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "norm_device.hpp"
+#include "norm_host.hpp"
+
+namespace mi355norm {
+
+constexpr int kAdBlock = 256;
+constexpr int kAdUnroll = 4;  // vectors per thread
+
+struct AdArgs {
+    int64_t n;           // elements
+    uint32_t k0, k1;     // Philox key (seed)
+    uint64_t blk0;       // offset / 4: the counter of element 0's word group
+    uint32_t thresh;     // drop when (word >> 8) < thresh
+    float scale;         // 1 / (1 - p)
+    int act_rt;          // activation for the run-time dispatched instance
+    float act_p;         // its parameter
+};
+
+// Philox4x32-10 on counter (c0, c1, 0, 0): ten rounds of the published
+// round function, the key bumped by the Weyl constants between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1,
+                                              uint32_t w[4]) {
+    uint32_t c2 = 0u, c3 = 0u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        // One 32 x 32 -> 64-bit product per multiplier (v_mad_u64_u32)
+        // instead of separate high and low multiplies.
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        const uint32_t n0 = hi1 ^ c1 ^ k0;
+        const uint32_t n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    w[0] = c0;
+    w[1] = c1;
+    w[2] = c2;
+    w[3] = c3;
+}
+
+// Keep flags of the V elements of vector vi (V = 4 or 8), or of element vi
+// for V = 1.
+template <int V>
+__device__ __forceinline__ void keep_flags(const AdArgs &a, int64_t vi, bool keep[V]) {
+    if constexpr (V == 1) {
+        const uint64_t blk = a.blk0 + (uint64_t)(vi >> 2);
+        uint32_t w[4];
+        philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), a.k0, a.k1, w);
+        keep[0] = (w[vi & 3] >> 8) >= a.thresh;
+    } else {
+#pragma unroll
+        for (int g = 0; g < V / 4; ++g) {
+            const uint64_t blk = a.blk0 + (uint64_t)vi * (V / 4) + g;
+            uint32_t w[4];
+            philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), a.k0, a.k1, w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) keep[g * 4 + e] = (w[e] >> 8) >= a.thresh;
+        }
+    }
+}
+
+// Forward over vectors v0, v0 + stride, ... below nvec, kAdUnroll loads in
+// flight (vector v holds elements v * V .. v * V + V - 1).  DROP = false is
+// the plain activation (p = 0: no generator calls).
+template <typename T, int V, int ACT, bool DROP>
+__device__ __forceinline__ void ad_fwd_range(const T *__restrict__ x, T *__restrict__ y, int64_t nvec,
+                                             int64_t v0, int64_t stride, const AdArgs &a) {
+    using VT = Vec<T, V>;
+    using raw_t = typename VT::raw_t;
+    constexpr bool kFast = std::is_same<T, bf16_t>::value;
+    for (int64_t vb = v0; vb < nvec; vb += stride * kAdUnroll) {
+        raw_t r[kAdUnroll];
+#pragma unroll
+        for (int u = 0; u < kAdUnroll; ++u) {
+            const int64_t v = vb + u * stride;
+            if (v < nvec) r[u] = vload_stream<T, V>(x + v * V);
+        }
+#pragma unroll
+        for (int u = 0; u < kAdUnroll; ++u) {
+            const int64_t v = vb + u * stride;
+            if (v < nvec) {
+                float f[V], o[V];
+                VT::unpack(r[u], f);
+                bool keep[V];
+                if (DROP) keep_flags<V>(a, v, keep);
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float t = act_fwd_any<ACT, kFast>(f[e], a.act_rt, a.act_p);
+                    o[e] = DROP ? (keep[e] ? t * a.scale : 0.0f) : t;
+                }
+                vstore_stream<T, V>(y + v * V, VT::pack(o));
+            }
+        }
+    }
+}
+
+template <typename T, int V, int ACT, bool DROP>
+__device__ __forceinline__ void ad_bwd_range(const T *__restrict__ dy, const T *__restrict__ x,
+                                             T *__restrict__ dx, int64_t nvec, int64_t v0, int64_t stride,
+                                             const AdArgs &a) {
+    using VT = Vec<T, V>;
+    using raw_t = typename VT::raw_t;
+    constexpr bool kFast = sizeof(T) == 2;
+    for (int64_t vb = v0; vb < nvec; vb += stride * kAdUnroll) {
+        raw_t rd[kAdUnroll], rx[kAdUnroll];
+#pragma unroll
+        for (int u = 0; u < kAdUnroll; ++u) {
+            const int64_t v = vb + u * stride;
+            if (v < nvec) {
+                rd[u] = vload_stream<T, V>(dy + v * V);
+                rx[u] = vload_stream<T, V>(x + v * V);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kAdUnroll; ++u) {
+            const int64_t v = vb + u * stride;
+            if (v < nvec) {
+                float df[V], xf[V], o[V];
+                VT::unpack(rd[u], df);
+                VT::unpack(rx[u], xf);
+                bool keep[V];
+                if (DROP) keep_flags<V>(a, v, keep);
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float g = df[e] * act_grad_any<ACT, kFast>(xf[e], a.act_rt, a.act_p);
+                    o[e] = DROP ? (keep[e] ? g * a.scale : 0.0f) : g;
+                }
+                vstore_stream<T, V>(dx + v * V, VT::pack(o));
+            }
+        }
+    }
+}
+
+// One launch covers the n / V full vectors (V-wide path) and the n mod V
+// tail elements (scalar, by the first threads of the grid).
+template <typename T, int V, int ACT, bool DROP>
+__global__ void __launch_bounds__(kAdBlock)
+act_dropout_fwd_kernel(const T *__restrict__ x, T *__restrict__ y, AdArgs a) {
+    const int64_t nvec = a.n / V;
+    const int64_t t0 = (int64_t)blockIdx.x * kAdBlock * kAdUnroll + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kAdBlock * kAdUnroll;
+    // Each block covers kAdUnroll * kAdBlock consecutive vectors per pass.
+    for (int64_t base = (int64_t)blockIdx.x * kAdBlock * kAdUnroll; base < nvec; base += stride)
+        ad_fwd_range<T, V, ACT, DROP>(x, y, base + kAdBlock * kAdUnroll < nvec ? base + kAdBlock * kAdUnroll : nvec,
+                                      base + threadIdx.x, kAdBlock, a);
+    if (V > 1) {
+        const int64_t tail = a.n - nvec * V;
+        if (t0 < tail) {
+            const int64_t i = nvec * V + t0;
+            ad_fwd_range<T, 1, ACT, DROP>(x, y, i + 1, i, 1, a);
+        }
+    }
+}
+
+template <typename T, int V, int ACT, bool DROP>
+__global__ void __launch_bounds__(kAdBlock)
+act_dropout_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ dx, AdArgs a) {
+    const int64_t nvec = a.n / V;
+    const int64_t t0 = (int64_t)blockIdx.x * kAdBlock * kAdUnroll + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kAdBlock * kAdUnroll;
+    for (int64_t base = (int64_t)blockIdx.x * kAdBlock * kAdUnroll; base < nvec; base += stride)
+        ad_bwd_range<T, V, ACT, DROP>(dy, x, dx, base + kAdBlock * kAdUnroll < nvec ? base + kAdBlock * kAdUnroll : nvec,
+                                      base + threadIdx.x, kAdBlock, a);
+    if (V > 1) {
+        const int64_t tail = a.n - nvec * V;
+        if (t0 < tail) {
+            const int64_t i = nvec * V + t0;
+            ad_bwd_range<T, 1, ACT, DROP>(dy, x, dx, i + 1, i, 1, a);
+        }
+    }
+}
+
+// Launchers (instantiated per dtype in ad_inst.hip).
+template <typename T, int V> norm_status ad_launch_fwd(const AdArgs &a, const void *x, void *y, hipStream_t s);
+template <typename T, int V>
+norm_status ad_launch_bwd(const AdArgs &a, const void *dy, const void *x, void *dx, hipStream_t s);
+
+}  // namespace mi355norm

@@ -177,14 +177,6 @@ static norm_status run(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, BnOp op
     });
 }
 
-static bool act_ok(norm_act a) { return (int)a >= 0 && (int)a < kActCount; }
-
-// The activation parameter must be finite; CELU divides by it.
-static bool act_param_ok(norm_act a, float p) {
-    if (!(p == p) || p == __builtin_inff() || p == -__builtin_inff()) return false;
-    return !(a == NORM_ACT_CELU && p == 0.0f);
-}
-
 }  // namespace mi355norm
 
 using namespace mi355norm;

@@ -61,4 +61,12 @@ inline norm_status launch_status() {
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Activation argument checks shared by the entry points: a known
+// activation, and a finite parameter (nonzero for CELU, which divides by it).
+inline bool act_ok(norm_act a) { return (int)a >= 0 && (int)a < kActCount; }
+inline bool act_param_ok(norm_act a, float p) {
+    if (!(p == p) || p == __builtin_inff() || p == -__builtin_inff()) return false;
+    return !(a == NORM_ACT_CELU && p == 0.0f);
+}
+
 }  // namespace mi355norm

@@ -1,5 +1,6 @@
 """Drop-in PyTorch layers over the C ABI: LayerNorm, RMSNorm, BatchNorm1d and
-BatchNorm2d with a fused residual add and activation.
+BatchNorm2d with a fused residual add and activation, and a fused
+activation + dropout.
 
 Pages (by title):
   [NormPage] "How attorch implements LayerNorm, BatchNorm and RMSNorm: the
@@ -279,6 +280,53 @@ class BatchNorm2d(_FusedBatchNorm, nn.BatchNorm2d):
                                 track_running_stats=track_running_stats, device=device,
                                 dtype=dtype)
         self._init_act(act_func)
+
+
+# ------------------------------------------------------ activation + dropout
+class _ActDropoutFn(torch.autograd.Function):
+    @staticmethod
+    @torch.amp.custom_fwd(device_type="cuda")
+    def forward(ctx, x, act, act_param, p, seed):
+        x = x.contiguous()
+        y = nl.act_dropout_fwd(x, act, p, seed, 0, act_param=act_param)
+        ctx.save_for_backward(x)
+        ctx.cfg = (act, act_param, p, seed)
+        return y
+
+    @staticmethod
+    @torch.amp.custom_bwd(device_type="cuda")
+    def backward(ctx, dy):
+        (x,) = ctx.saved_tensors
+        act, act_param, p, seed = ctx.cfg
+        dx = nl.act_dropout_bwd(dy.to(x.dtype).contiguous(), x, act, p, seed, 0, act_param=act_param)
+        return dx, None, None, None, None
+
+
+class ActDropout(nn.Module):
+    """An activation followed by inverted dropout in one kernel ([ActPage]
+    sections 3-5), e.g. ActDropout("gelu", drop_p=0.1).  Training draws a
+    64-bit seed from PyTorch's default CPU generator per call (kept in
+    `last_seed`); the backward regenerates the mask from it instead of
+    storing it.  In eval mode (or with drop_p = 0) it is the plain
+    activation."""
+
+    def __init__(self, act_func="relu", drop_p=0.5):
+        super().__init__()
+        if not 0.0 <= drop_p <= 1.0:
+            raise ValueError("drop_p must be in [0, 1]")
+        self.act_func = act_func
+        self._act, self._act_param = parse_act(act_func)
+        self.drop_p = float(drop_p)
+        self.last_seed = None
+
+    def forward(self, x):
+        p = self.drop_p if self.training else 0.0
+        seed = int(torch.randint(0, 1 << 62, (1,)).item()) if p > 0.0 else 0
+        self.last_seed = seed
+        return _ActDropoutFn.apply(x, self._act, self._act_param, p, seed)
+
+    def extra_repr(self):
+        return f"act_func={self.act_func!r}, drop_p={self.drop_p}"
 
 
 def output_dtype(input_dtype, autocast_enabled, autocast_to_fp32=True, kind="layer_norm"):

@@ -30,6 +30,7 @@ _I64 = ctypes.c_int64
 _I = ctypes.c_int
 _F = ctypes.c_float
 _SZ = ctypes.c_size_t
+_U64 = ctypes.c_uint64
 
 SIGNATURES = {
     "ln_fwd": (_I, [_I, _I64, _I64, _F, _V, _V, _V, _V, _V, _V, _V]),
@@ -44,6 +45,8 @@ SIGNATURES = {
     "bn_fwd_eval": (_I, [_I, _I64, _I64, _I64, _F, _I, _F, _V, _V, _V, _V, _V, _V, _V, _V]),
     "bn_bwd": (_I, [_I, _I64, _I64, _I64, _I, _F, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V, _V,
                     _SZ, _V]),
+    "act_dropout_fwd": (_I, [_I, _I64, _I, _F, _F, _U64, _U64, _V, _V, _V]),
+    "act_dropout_bwd": (_I, [_I, _I64, _I, _F, _F, _U64, _U64, _V, _V, _V, _V]),
     "norm_status_str": (ctypes.c_char_p, [_I]),
     "norm_arm_kernel_events": (None, [ctypes.POINTER(ctypes.c_void_p), _I]),
     "norm_last_kernel_count": (_I, []),
@@ -279,3 +282,29 @@ def bn_bwd(dy, x, w, b, save_mean, save_rstd, act="none", res=None, *, act_param
         _ptr(save_mean), _ptr(save_rstd), _ptr(dx), _ptr(dres), _ptr(dw), _ptr(db), _ptr(ws),
         nbytes, _stream(x.device)))
     return dx, dres, dw, db
+
+
+# ------------------------------------------------------ activation + dropout
+def act_dropout_fwd(x, act="none", drop_p=0.0, seed=0, offset=0, *, act_param=0.0, y=None):
+    """y = act(x) with inverted dropout (probability drop_p), element-wise;
+    the mask is a function of (seed, offset + element index)."""
+    y = torch.empty_like(x) if y is None else y
+    _same(y, x, "y")
+    if y.numel() != x.numel():
+        raise ValueError("y must have x's size")
+    _check("act_dropout_fwd", lib().act_dropout_fwd(
+        _dt(x), x.numel(), ACT[act], float(act_param), float(drop_p), int(seed), int(offset),
+        _ptr(x), _ptr(y), _stream(x.device)))
+    return y
+
+
+def act_dropout_bwd(dy, x, act="none", drop_p=0.0, seed=0, offset=0, *, act_param=0.0, dx=None):
+    """dx = dy * act'(x) through the same dropout mask as the forward."""
+    _same(dy, x, "dy")
+    dx = torch.empty_like(x) if dx is None else dx
+    if dy.numel() != x.numel() or dx.numel() != x.numel():
+        raise ValueError("dy, x and dx must have the same size")
+    _check("act_dropout_bwd", lib().act_dropout_bwd(
+        _dt(x), x.numel(), ACT[act], float(act_param), float(drop_p), int(seed), int(offset),
+        _ptr(dy), _ptr(x), _ptr(dx), _stream(x.device)))
+    return dx

@@ -40,9 +40,11 @@ The six workloads (sizes as the benchmark runs them):
                          running variance 1 at the start
 
 EXTRA_WORKLOADS adds fp16 variants of the RMSNorm and bf16 BatchNorm
-workloads and two BatchNorm1d workloads (same recipe as the BatchNorm2d
-ones): (N, C) = 8192 x 2048 fp32 with ReLU, and (N, C, L) = 2048 x 512 x 32
-bf16 with residual + GELU and an eval step.
+workloads, two BatchNorm1d workloads (same recipe as the BatchNorm2d ones):
+(N, C) = 8192 x 2048 fp32 with ReLU, and (N, C, L) = 2048 x 512 x 32 bf16
+with residual + GELU and an eval step, and an activation + dropout workload:
+x, dy ~ N(0, 1) of 16384 x 4096 bf16, GELU, drop probability 0.1, a fixed
+64-bit dropout seed.
 """
 from dataclasses import dataclass, field
 
@@ -52,7 +54,7 @@ import numpy as np
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "ln", "rms" or "bn"
+    kind: str            # "ln", "rms", "bn" or "ad" (activation + dropout)
     dtype: str           # "f32", "bf16" or "f16" (I/O dtype)
     shape: tuple         # (M, N) for ln/rms, (N, C, H, W) for bn
     seed: int
@@ -115,6 +117,8 @@ EXTRA_WORKLOADS = {
         Workload("bn1d_bf16_2048x512x32", "bn", "bf16", (2048, 512, 32, 1), 1006, 1e-5,
                  momentum=0.1, act="gelu", residual=True, eval_after_train=True,
                  extra=dict(mu_range=(-1.0, 1.0), sd_range=(0.2, 4.0))),
+        Workload("actdrop_bf16_16384x4096", "ad", "bf16", (16384, 4096), 1007, 0.0,
+                 act="gelu", extra=dict(drop_p=0.1, dropout_seed=0x5EED1234ABCD, x_std=1.0)),
     ]
 }
 
@@ -197,3 +201,13 @@ def gen_bn(wl: Workload, Nb: int = None, C: int = None, HW: int = None, seed: in
     return dict(x=to_io(x, wl.dtype), res=to_io(res, wl.dtype) if res is not None else None,
                 w=to_io(w, wl.dtype), b=to_io(b, wl.dtype), dy=to_io(dy, wl.dtype),
                 running_mean=np.zeros(C, np.float32), running_var=np.ones(C, np.float32))
+
+
+def gen_act_dropout(wl: Workload, n: int = None, seed: int = None):
+    """Inputs for an activation + dropout workload: dict(x, dy), flat, in the
+    workload's I/O dtype; x ~ N(0, x_std), dy ~ N(0, 1)."""
+    n = wl.shape[0] * wl.shape[1] if n is None else n
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    x = _normal(rng, (n,), std=wl.extra.get("x_std", 1.0))
+    dy = _normal(rng, (n,))
+    return dict(x=to_io(x, wl.dtype), dy=to_io(dy, wl.dtype))

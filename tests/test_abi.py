@@ -38,7 +38,8 @@ def test_header_declares_the_entry_points():
     for n in ["ln_fwd", "ln_bwd", "ln_bwd_workspace_bytes", "rms_fwd", "rms_bwd",
               "rms_bwd_workspace_bytes", "bn_workspace_bytes", "bn_fwd_train", "bn_fwd_eval",
               "bn_bwd", "norm_status_str", "norm_arm_kernel_events", "norm_last_kernel_count",
-              "norm_last_kernel_name", "norm_last_main_kernel"]:
+              "norm_last_kernel_name", "norm_last_main_kernel", "act_dropout_fwd",
+              "act_dropout_bwd"]:
         assert n in names, n
 
 
@@ -155,3 +156,23 @@ def test_timing_hook_bookkeeping_without_gpu(lib):
     assert lib.norm_last_main_kernel() == -1
     assert lib.norm_last_kernel_name(0) == b""
     lib.norm_arm_kernel_events(None, 0)
+
+
+def test_act_dropout_errors(lib):
+    fwd = lambda **k: lib.act_dropout_fwd(*[k.get(n, d) for n, d in (
+        ("dt", F32), ("n", 16), ("act", 2), ("ap", 0.0), ("p", 0.1), ("seed", 1), ("off", 0),
+        ("x", P), ("y", P), ("s", NULL))])
+    assert fwd(dt=3) == EDTYPE
+    assert fwd(n=-1) == ESHAPE
+    assert fwd(act=15) == EACT
+    assert fwd(act=10, ap=0.0) == EARG
+    for bad in (-0.1, 1.5, float("nan")):
+        assert fwd(p=bad) == EARG
+    assert fwd(off=2) == EARG  # the offset must be a multiple of 4
+    assert fwd(off=(1 << 64) - 4) == EARG  # offset + n overflows
+    assert fwd(x=NULL) == ENULL
+    assert fwd(y=NULL) == ENULL
+    assert fwd(n=0, x=NULL, y=NULL) == OK
+    assert lib.act_dropout_bwd(F32, 16, 0, 0.0, 0.5, 1, 0, P, NULL, P, NULL) == ENULL
+    assert lib.act_dropout_bwd(F32, 16, 0, 0.0, 0.5, 1, 6, P, P, P, NULL) == EARG
+    assert lib.act_dropout_bwd(BF16, 0, 0, 0.0, 0.5, 1, 0, NULL, NULL, NULL, NULL) == OK

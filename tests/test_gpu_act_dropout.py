@@ -1,0 +1,124 @@
+"""GPU parity of the fused activation + dropout against the float64 oracle:
+the keep mask bit for bit (an integer decision on the generator's words,
+taken identically on both sides), y and dx element by element, the edge
+probabilities, split calls with offsets, unaligned tensors, and the full
+16384 x 4096 bf16 workload."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from tests._parity import check, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+nl = pytest.importorskip("normalization_ln_rmsnorm_amd")
+from normalization_ln_rmsnorm_amd.workloads import EXTRA_WORKLOADS, gen_act_dropout  # noqa: E402
+
+WL = EXTRA_WORKLOADS["actdrop_bf16_16384x4096"]
+
+
+def _inputs(dtype, n, seed):
+    return gen_act_dropout(dataclasses.replace(WL, dtype=dtype), n=n, seed=seed)
+
+
+def run_case(orc, dtype, n, act, p, seed, offset, param=0.0, x_dev=None):
+    inp = _inputs(dtype, n, seed=(seed ^ n) & 0xFFFF)
+    bf16 = dtype == "bf16"
+    x = to_dev(inp["x"], dtype) if x_dev is None else x_dev(inp["x"])
+    dy = to_dev(inp["dy"], dtype)
+    p32 = float(np.float32(p))  # the kernels see p as float32
+    y = nl.act_dropout_fwd(x, act, p, seed, offset, act_param=param)
+    ynone = nl.act_dropout_fwd(x, "none", p, seed, offset)
+    dx = nl.act_dropout_bwd(dy, x, act, p, seed, offset, act_param=param)
+    torch.cuda.synchronize()
+    keep = orc.dropout_keep(n, p32, seed, offset)
+    # x has no exact zeros, so the identity activation exposes the mask.
+    assert (orc.widen(inp["x"], bf16=bf16) != 0).all()
+    got_keep = (to_f64(ynone) != 0).astype(np.uint8)
+    mism = np.flatnonzero(got_keep != keep)
+    assert mism.size == 0, f"mask differs at {mism[:8]} (of {mism.size})"
+    tag = f"ad/{dtype}/n={n}/{act}({param})/p={p}/seed={seed}/off={offset}"
+    ry = orc.act_dropout_fwd(inp["x"], act, p32, seed, offset, act_param=param, bf16=bf16)
+    rdx = orc.act_dropout_bwd(inp["dy"], inp["x"], act, p32, seed, offset, act_param=param, bf16=bf16)
+    check(f"{tag} y", to_f64(y), ry, dtype)
+    check(f"{tag} dx", to_f64(dx), rdx, dtype)
+    return y, dx
+
+
+ACTS = [("none", 0.0), ("relu", 0.0), ("gelu", 0.0), ("silu", 0.0), ("leaky_relu", 0.2),
+        ("hardswish", 0.0), ("tanh", 0.0)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("act,param", ACTS)
+@pytest.mark.parametrize("n", [1, 3, 8, 1000, 4099, (1 << 16) + 5])
+def test_parity(orc, dtype, act, param, n):
+    print(f"case act_dropout {dtype} {act} n={n}", flush=True)
+    run_case(orc, dtype, n, act, 0.1, seed=0x1234_5678_9ABC, offset=0, param=param)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("p", [0.0, 0.5, 0.9, 1.0])
+@pytest.mark.parametrize("offset", [0, 4, 1 << 34])
+def test_probabilities_and_offsets(orc, dtype, p, offset):
+    print(f"case act_dropout {dtype} p={p} offset={offset}", flush=True)
+    if p in (0.0, 1.0):
+        # p = 0 keeps everything (the plain activation); p = 1 drops all.
+        n = 5000
+        inp = _inputs(dtype, n, 1)
+        x = to_dev(inp["x"], dtype)
+        y = nl.act_dropout_fwd(x, "gelu", p, 77, offset)
+        torch.cuda.synchronize()
+        ref = orc.act("gelu", orc.widen(inp["x"], bf16=dtype == "bf16")) if p == 0.0 else np.zeros(n)
+        check(f"p={p} y", to_f64(y), ref, dtype)
+        return
+    run_case(orc, dtype, 20000, "gelu", p, seed=(1 << 40) + 3, offset=offset)
+
+
+def test_split_calls_reproduce_the_whole(orc):
+    """Two calls with offsets give the mask and values of one call."""
+    n, n1 = 10000, 4096
+    x = to_dev(_inputs("f32", n, 9)["x"], "f32")
+    whole = nl.act_dropout_fwd(x, "silu", 0.3, 42, 0)
+    a = nl.act_dropout_fwd(x[:n1].contiguous(), "silu", 0.3, 42, 0)
+    b = nl.act_dropout_fwd(x[n1:].contiguous(), "silu", 0.3, 42, n1)
+    torch.cuda.synchronize()
+    assert torch.equal(whole, torch.cat([a, b]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unaligned_tensors_take_the_scalar_path(orc, dtype):
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+
+    def shifted(a):
+        t = to_dev(a, dtype)
+        big = torch.empty(t.numel() + 1, dtype=tdt, device="cuda")
+        big[1:].copy_(t)
+        return big[1:]
+    run_case(orc, dtype, 3001, "gelu", 0.25, seed=5, offset=8, x_dev=shifted)
+
+
+def test_full_size_workload(orc):
+    M, N = WL.shape
+    print("case actdrop_bf16_16384x4096", flush=True)
+    inp = gen_act_dropout(WL)
+    x, dy = to_dev(inp["x"], "bf16"), to_dev(inp["dy"], "bf16")
+    p, seed = WL.extra["drop_p"], WL.extra["dropout_seed"]
+    y = nl.act_dropout_fwd(x, WL.act, p, seed, 0)
+    dx = nl.act_dropout_bwd(dy, x, WL.act, p, seed, 0)
+    torch.cuda.synchronize()
+    p32 = float(np.float32(p))
+    ry = orc.act_dropout_fwd(inp["x"], WL.act, p32, seed, 0, bf16=True)
+    check("full y", to_f64(y), ry, "bf16")
+    del ry
+    rdx = orc.act_dropout_bwd(inp["dy"], inp["x"], WL.act, p32, seed, 0, bf16=True)
+    check("full dx", to_f64(dx), rdx, "bf16")
+    keep = orc.dropout_keep(M * N, p32, seed, 0)
+    # GELU(x) = 0 only at x = 0 (the draw holds a few exact zeros): dropped
+    # elements are 0 and, wherever x != 0, kept ones are not.
+    yv = to_f64(y)
+    nz = orc.widen(inp["x"], bf16=True) != 0
+    assert (yv[keep == 0] == 0).all()
+    assert np.array_equal((yv[nz] != 0).astype(np.uint8), keep[nz])

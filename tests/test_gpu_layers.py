@@ -222,3 +222,27 @@ def test_eval_mode_backward_is_refused():
     x = torch.randn(2, 4, 3, 3, device="cuda", requires_grad=True)
     with pytest.raises(NotImplementedError):
         bn(x).sum().backward()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_act_dropout_layer(orc, dtype):
+    from normalization_ln_rmsnorm_amd.workloads import EXTRA_WORKLOADS, gen_act_dropout
+    wl = dataclasses.replace(EXTRA_WORKLOADS["actdrop_bf16_16384x4096"], dtype=dtype)
+    inp = gen_act_dropout(wl, n=6 * 1000, seed=4)
+    torch.manual_seed(123)
+    m = nm.ActDropout("leaky_relu_0.1", drop_p=0.3)
+    x = to_dev(inp["x"], dtype).view(6, 1000).requires_grad_(True)
+    y = m(x)
+    y.backward(to_dev(inp["dy"], dtype).view(6, 1000))
+    torch.cuda.synchronize()
+    p32 = float(np.float32(0.3))
+    ry = orc.act_dropout_fwd(inp["x"], "leaky_relu", p32, m.last_seed, 0, act_param=0.1, bf16=_bf(dtype))
+    rdx = orc.act_dropout_bwd(inp["dy"], inp["x"], "leaky_relu", p32, m.last_seed, 0, act_param=0.1,
+                              bf16=_bf(dtype))
+    check("ActDropout y", to_f64(y).ravel(), ry, dtype)
+    check("ActDropout dx", to_f64(x.grad).ravel(), rdx, dtype)
+    m.eval()
+    ye = m(x.detach())
+    torch.cuda.synchronize()
+    check("ActDropout eval", to_f64(ye).ravel(),
+          orc.act("leaky_relu", orc.widen(inp["x"], bf16=_bf(dtype)), param=0.1), dtype)

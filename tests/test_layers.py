@@ -55,3 +55,12 @@ def test_output_dtype_policy():
     assert nm.output_dtype(bf, True, autocast_to_fp32=False) == bf
     assert nm.output_dtype(bf, False) == bf
     assert nm.output_dtype(bf, True, kind="batch_norm") == bf
+
+
+def test_act_dropout_module_checks():
+    with pytest.raises(ValueError):
+        nm.ActDropout("gelu", drop_p=1.5)
+    with pytest.raises(ValueError):
+        nm.ActDropout("nope", drop_p=0.1)
+    with pytest.raises(ValueError, match="GPU"):
+        nm.ActDropout("gelu", drop_p=0.1)(torch.randn(8))
