@@ -6,13 +6,16 @@
 A step is one forward and one backward pass of the workload (BatchNorm
 workloads: training forward, backward, and the eval forward when the workload
 has one) on seeded synthetic inputs already resident in HBM.  Before every
-operation a 512 MiB scratch buffer is written, so inputs come from HBM rather
-than the 256 MB Infinity Cache; that flush is outside the timed spans.  Each
+operation a 512 MiB scratch buffer is streamed (read by default, --flush
+write rewrites it), so inputs come from HBM rather than the 256 MB Infinity
+Cache; that flush is outside the timed spans.  Each
 operation is timed on the device: the library attaches caller-created HIP
-events to its kernels' own dispatches (norm_arm_kernel_events), so an
-operation's time runs from its first kernel's start to its last kernel's end
-and the main streaming kernel's duration is measured by itself -- the same
-quantities rocprofv3's kernel trace reports.  Host-side events around each
+events to its kernels' own dispatches (norm_arm_kernel_events).  A span pass
+with events only on the first kernel's start and the last kernel's end gives
+the operation's time (events between kernels would delay the next dispatch);
+a second pass with events on every kernel gives each kernel's duration, the
+main streaming kernel's for the roofline -- the same quantities rocprofv3's
+kernel trace reports.  Host-side events around each
 call are recorded too (they add the ~6 us dispatch latency of a lone launch).
 
 Bytes are algorithmic: what the method must move (every activation tensor in
@@ -49,6 +52,8 @@ def parse():
     p.add_argument("--other-steps", type=int, default=20)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--flush", choices=["read", "write"], default="read",
+                   help="evict the caches by reading (default) or rewriting a 512 MiB buffer")
     return p.parse_args()
 
 
@@ -69,6 +74,11 @@ class Hip:
         if rc != 0:
             raise RuntimeError(f"hipEventCreate failed ({rc})")
         return ev
+
+    def destroy(self, events):
+        for e in events:
+            if e is not None:
+                self.lib.hipEventDestroy(e)
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -250,28 +260,63 @@ def bench_class(wl):
 MAX_KERNELS = 4  # kernels per operation timed through the library's hook
 
 
+class CacheFlush:
+    """Evicts the 256 MB Infinity Cache and the L2s before each operation by
+    streaming a 512 MiB buffer: read (a sum into a scalar; leaves no dirty
+    lines whose write-back the next kernel would share HBM with) or
+    rewritten in place."""
+
+    def __init__(self, torch, mode):
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.empty((), dtype=torch.float32, device="cuda")
+        self.mode = mode
+        self.torch = torch
+
+    def add_(self, _=None):
+        if self.mode == "read":
+            self.torch.sum(self.buf, dim=0, out=self.sink)
+        else:
+            self.buf.add_(1)
+
+
 def measure(bench, steps, warmup, torch, hip, nl, flush):
-    """Runs `steps` timed steps.  Per operation it records (a) the device
-    span from its first kernel's start to its last kernel's end, via HIP
-    events the library attaches to the kernels' own dispatches, (b) the main
-    streaming kernel's own duration the same way, and (c) host-side events
-    around the call (adds dispatch latency)."""
+    """Runs `steps` timed steps; every operation runs twice per step (each
+    after the cache flush).  The span pass attaches HIP events only to the
+    first kernel's start and the last kernel's end (an event attached in
+    between delays the next dispatch by several microseconds, which plain
+    calls do not pay), giving the operation's device time.  The kernel pass
+    attaches a pair to every kernel, giving each kernel's own duration (the
+    main streaming kernel's for the roofline).  Host-side events around the
+    span pass are recorded too (they add the dispatch latency)."""
+    nk = {}
+    for op in bench.ops:  # kernel count of each operation
+        bench.run(op)
+        nk[op] = min(len(nl.last_kernels()[0]), MAX_KERNELS)
+    torch.cuda.synchronize()
+
     def one_step(record):
         out = {}
         for op in bench.ops:
             flush.add_(1)
-            if record:
-                evs = [hip.event() for _ in range(2 * MAX_KERNELS)]
-                nl.arm_kernel_events(evs)
-                h0 = torch.cuda.Event(enable_timing=True)
-                h1 = torch.cuda.Event(enable_timing=True)
-                h0.record()
+            if not record:
                 bench.run(op)
-                h1.record()
-                names, main = nl.last_kernels()
-                out[op] = (evs, names, main, h0, h1)
-            else:
-                bench.run(op)
+                continue
+            k = nk[op]
+            span = [hip.event(), hip.event()]
+            evs = [None] * (2 * k)
+            evs[0], evs[2 * k - 1] = span
+            nl.arm_kernel_events(evs)
+            h0 = torch.cuda.Event(enable_timing=True)
+            h1 = torch.cuda.Event(enable_timing=True)
+            h0.record()
+            bench.run(op)
+            h1.record()
+            flush.add_(1)
+            kev = [hip.event() for _ in range(2 * k)]
+            nl.arm_kernel_events(kev)
+            bench.run(op)
+            names, main = nl.last_kernels()
+            out[op] = (span, kev, names, main, h0, h1)
         return out
 
     for _ in range(warmup):
@@ -287,17 +332,20 @@ def measure(bench, steps, warmup, torch, hip, nl, flush):
         d, h, m = [], [], []
         per_kernel = None
         for r in recs:
-            evs, names, main, h0, h1 = r[op]
-            k = min(len(names), MAX_KERNELS)
-            d.append(hip.elapsed_ms(evs[0], evs[2 * k - 1]))
+            span, kev, names, main, h0, h1 = r[op]
+            k = nk[op]
+            d.append(hip.elapsed_ms(span[0], span[1]))
             h.append(h0.elapsed_time(h1))
-            m.append(hip.elapsed_ms(evs[2 * main], evs[2 * main + 1]) if main >= 0 else float("nan"))
-            ks = [hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(k)]
+            m.append(hip.elapsed_ms(kev[2 * main], kev[2 * main + 1]) if main >= 0 else float("nan"))
+            ks = [hip.elapsed_ms(kev[2 * i], kev[2 * i + 1]) for i in range(k)]
             per_kernel = [p + [t] for p, t in zip(per_kernel, ks)] if per_kernel else [[t] for t in ks]
             names_main[op] = (names, main)
         dev_ms[op], host_ms[op], main_ms[op] = d, h, m
         kern_ms[op] = {f"{i}:{names_main[op][0][i]}": float(np.mean(v)) * 1e3
                        for i, v in enumerate(per_kernel or [])}
+    for r in recs:
+        for span, kev, *_ in r.values():
+            hip.destroy(span + kev)
     return dict(dev=dev_ms, host=host_ms, main=main_ms, kernels_us=kern_ms, names=names_main,
                 wall=wall)
 
@@ -398,7 +446,7 @@ def main():
     torch.cuda.set_device(0)
     nl.lib()
     hip = Hip()
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    flush = CacheFlush(torch, args.flush)
 
     name = args.workload or HEADLINE
     every = {**WORKLOADS, **EXTRA_WORKLOADS}

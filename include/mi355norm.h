@@ -237,8 +237,12 @@ const char *norm_status_str(norm_status s);
  * events[2i+1] attached to that kernel's own dispatch (hipExtLaunchKernel),
  * so hipEventElapsedTime(events[2i], events[2i+1]) is the kernel's device
  * time, and (events[0], events[2k-1]) spans a k-kernel call from the first
- * kernel's start to the last kernel's end.  The call disarms the hook when
- * it returns.  Costs nothing when not armed.  n_pairs <= 0 disarms.        */
+ * kernel's start to the last kernel's end.  Either event of a pair may be
+ * NULL (that side is not recorded; a kernel whose pair is all NULL is
+ * launched plainly): an attached event delays the next dispatch by several
+ * microseconds, so a call's span is best taken with only events[0] and
+ * events[2k-1] set.  The call disarms the hook when it returns.  Costs
+ * nothing when not armed.  n_pairs <= 0 disarms.                          */
 void norm_arm_kernel_events(void *const *events, int n_pairs);
 
 /* Kernels launched by the last entry-point call on this host thread: their

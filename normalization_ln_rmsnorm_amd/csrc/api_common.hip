@@ -50,7 +50,7 @@ bool kernel_events(const char *name, bool is_main, hipEvent_t *start, hipEvent_t
         g_call.count = i + 1;
     }
     if (is_main) g_call.main_index = i;
-    if (i < g_call.armed_pairs && g_call.events[2 * i] && g_call.events[2 * i + 1]) {
+    if (i < g_call.armed_pairs && (g_call.events[2 * i] || g_call.events[2 * i + 1])) {
         *start = g_call.events[2 * i];
         *stop = g_call.events[2 * i + 1];
         return true;

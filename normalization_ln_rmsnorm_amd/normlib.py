@@ -135,8 +135,10 @@ def _workspace(nbytes, device, ws):
 
 def arm_kernel_events(events):
     """Arm hipEvent_t handles for the next call: kernel i of that call is
-    launched with events[2i] / events[2i+1] attached to its dispatch."""
-    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(getattr(e, "value", e)) for e in events])
+    launched with events[2i] / events[2i+1] attached to its dispatch (None
+    leaves that side unrecorded)."""
+    arr = (ctypes.c_void_p * len(events))(
+        *[ctypes.c_void_p(None if e is None else getattr(e, "value", e)) for e in events])
     lib().norm_arm_kernel_events(arr, len(events) // 2)
 
 
