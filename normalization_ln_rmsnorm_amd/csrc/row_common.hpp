@@ -29,7 +29,7 @@ norm_status row_launch_fwd(const RowPlan &p, hipStream_t s, const void *x, const
 template <typename T, bool RMS, int V>
 norm_status row_launch_bwd(const RowPlan &p, hipStream_t s, const void *dy, const void *x, const void *w,
                            const float *mean, const float *rstd, void *dx, float *part_w, float *part_b,
-                           int64_t M, int N);
+                           void *dw_out, void *db_out, int64_t M, int N);
 // dw / db from the partial rows (fixed order, float64); either may be NULL.
 template <typename T>
 void row_launch_colsum(hipStream_t s, const float *part_w, const float *part_b, int parts, int N, void *dw,

@@ -26,7 +26,8 @@ constexpr bool kRms = MI355NORM_ROW_RMS != 0;
                                                       int64_t, int, float);                                 \
     template norm_status row_launch_bwd<IoT, kRms, V>(const RowPlan &, hipStream_t, const void *,          \
                                                       const void *, const void *, const float *,            \
-                                                      const float *, void *, float *, float *, int64_t, int);
+                                                      const float *, void *, float *, float *, void *,   \
+                                                      void *, int64_t, int);
 
 MI355NORM_ROW_INST(kVW)
 MI355NORM_ROW_INST(1)

@@ -211,13 +211,16 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
 //   LayerNorm  dx = rstd * (g - mean_j(g) - xhat * mean_j(g * xhat))
 //   RMSNorm    dx = rstd * (g - xhat * mean_j(g * xhat))
 // (for RMSNorm, x * rstd^2 * mean_j(g * x) = xhat * mean_j(g * xhat)).
-// Column partials: dw += dy * xhat, db += dy, per thread, then per block.
+// Column partials: dw += dy * xhat, db += dy, per thread, then per block:
+// one float32 partial row per block into part_w / part_b, or, when the grid
+// is a single block, the final dw / db straight into dw_out / db_out (the
+// block's partial row is then the whole sum; no second kernel).
 template <typename T, int V, int IT, bool RMS, int MAXB>
 __global__ void __launch_bounds__(MAXB)
 row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__restrict__ w,
                const float *__restrict__ mean_in, const float *__restrict__ rstd_in,
                T *__restrict__ dx, float *__restrict__ part_w, float *__restrict__ part_b,
-               int64_t M, int N, float inv_n, int tpr) {
+               T *__restrict__ dw_out, T *__restrict__ db_out, int64_t M, int N, float inv_n, int tpr) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
     __shared__ float lds[2][kMaxWavesPerBlock][2];
@@ -351,7 +354,7 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
     // Combine the row slots of this block column by column and write one
     // partial row per block.  LDS layout [element][thread] avoids bank
     // conflicts; slots are added in increasing order.
-    if (part_w == nullptr && part_b == nullptr) return;
+    if (!part_w && !part_b && !dw_out && !db_out) return;
     if (rpb == 1) {  // one row slot: every thread owns distinct columns
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
@@ -362,6 +365,8 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
             for (int e = 0; e < V; ++e) {
                 if (part_w) part_w[off + e] = acc_w[k][e];
                 if (part_b) part_b[off + e] = acc_b[k][e];
+                if (dw_out) st1(dw_out + (off + e), acc_w[k][e]);
+                if (db_out) st1(db_out + (off + e), acc_b[k][e]);
             }
         }
         return;
@@ -372,7 +377,8 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
     extern __shared__ float colbuf[];  // rpb * N floats
     for (int which = 0; which < 2; ++which) {
         float *part = which == 0 ? part_w : part_b;
-        if (part == nullptr) continue;
+        T *out = which == 0 ? dw_out : db_out;
+        if (part == nullptr && out == nullptr) continue;
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
@@ -387,7 +393,10 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
         for (int col = threadIdx.x; col < N; col += blockDim.x) {
             float sum = 0.0f;
             for (int r = 0; r < rpb; ++r) sum += colbuf[r * N + col];
-            part[(int64_t)blockIdx.x * N + col] = sum;
+            if (out)
+                st1(out + col, sum);
+            else
+                part[(int64_t)blockIdx.x * N + col] = sum;
         }
     }
 }
@@ -463,9 +472,9 @@ norm_status row_launch_fwd(const RowPlan &p, hipStream_t s, const void *x, const
 template <typename T, bool RMS, int V>
 norm_status row_launch_bwd(const RowPlan &p, hipStream_t s, const void *dy, const void *x, const void *w,
                            const float *mean, const float *rstd, void *dx, float *part_w, float *part_b,
-                           int64_t M, int N) {
+                           void *dw_out, void *db_out, int64_t M, int N) {
     using fn_t = void (*)(const T *, const T *, const T *, const float *, const float *, T *,
-                          float *, float *, int64_t, int, float, int);
+                          float *, float *, T *, T *, int64_t, int, float, int);
     fn_t fn = nullptr;
     switch (p.it) {
     case 1: fn = p.block > 256 ? row_bwd_kernel<T, V, 1, RMS, 1024> : row_bwd_kernel<T, V, 1, RMS, 256>; break;
@@ -480,11 +489,12 @@ norm_status row_launch_bwd(const RowPlan &p, hipStream_t s, const void *dy, cons
     }
     if (!fn) return NORM_ERR_SHAPE;
     const int rpb = p.block / p.tpr;
-    const size_t shmem = ((part_w || part_b) && rpb > 1) ? (size_t)rpb * N * sizeof(float) : 0;
+    const bool sums = part_w || part_b || dw_out || db_out;
+    const size_t shmem = (sums && rpb > 1) ? (size_t)rpb * N * sizeof(float) : 0;
     if (shmem > 65536) return NORM_ERR_SHAPE;  // only reachable through the tuning override
     launch(RMS ? "row_bwd_kernel<rms>" : "row_bwd_kernel<ln>", true, fn, dim3(p.grid), dim3(p.block), shmem, s,
-           (const T *)dy, (const T *)x, (const T *)w, mean, rstd, (T *)dx, part_w, part_b, M, N,
-           1.0f / (float)N, p.tpr);
+           (const T *)dy, (const T *)x, (const T *)w, mean, rstd, (T *)dx, part_w, part_b, (T *)dw_out,
+           (T *)db_out, M, N, 1.0f / (float)N, p.tpr);
     return launch_status();
 }
 

@@ -17,6 +17,8 @@
 
 namespace mi355norm {
 
+constexpr int64_t kDirectRowGroups = 8;  // backward: one block (no column-sum kernel) up to this
+
 // ---------------------------------------------------------------- planning
 
 
@@ -86,8 +88,15 @@ static bool make_plan(norm_dtype dt, int64_t M, int64_t N, bool vec_ok, bool bac
     const int rpb = p->block / p->tpr;
     // The backward writes one partial row of dw (and db) per block, so a
     // block should cover at least two row groups; the forward has no
-    // partials and takes one block per row group.
-    const int64_t needed = backward ? ceil_div(M, 2 * (int64_t)rpb) : ceil_div(M, rpb);
+    // partials and takes one block per row group.  A backward of at most
+    // kDirectRowGroups row groups runs as one block that writes dw / db
+    // itself: a few extra row iterations cost less than the column-sum
+    // kernel and its launch.
+    const int64_t groups = ceil_div(M, rpb);
+    // (Widening that block to 1024 threads to cut its row passes measured
+    // 2.8x slower on LayerNorm 64 x 256.)
+    const bool direct = backward && groups <= kDirectRowGroups;
+    const int64_t needed = direct ? 1 : backward ? ceil_div(M, 2 * (int64_t)rpb) : groups;
     const int64_t cap = (int64_t)device_cu_count() * bpc;
     p->grid = (int)(needed < cap ? needed : cap);
     if (p->grid < 1) p->grid = 1;
@@ -175,14 +184,22 @@ static norm_status bwd_entry(norm_dtype dt, int64_t M, int64_t N, const void *dy
     const bool vec = row_vec_ok(dt, N, {dy, x, w, dx});
     RowPlan p;
     if (!make_plan(dt, M, N, vec, true, &p)) return NORM_ERR_SHAPE;
-    float *part_w = dw ? static_cast<float *>(ws) : nullptr;
-    float *part_b = (!RMS && db) ? static_cast<float *>(ws) + (size_t)max_partial_rows(M) * N : nullptr;
+    // One block: it writes dw / db directly.  Otherwise float32 partial
+    // rows in the workspace, added by the column-sum kernel.
+    const bool direct = p.grid == 1;
+    float *part_w = (dw && !direct) ? static_cast<float *>(ws) : nullptr;
+    float *part_b = (!RMS && db && !direct) ? static_cast<float *>(ws) + (size_t)max_partial_rows(M) * N
+                                            : nullptr;
+    void *dw_out = direct ? dw : nullptr;
+    void *db_out = (direct && !RMS) ? db : nullptr;
     return with_io_type(dt, [&](auto tag) {
         using T = typename decltype(tag)::type;
         constexpr int VW = 16 / (int)sizeof(T);
-        norm_status r = vec ? row_launch_bwd<T, RMS, VW>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n)
-                            : row_launch_bwd<T, RMS, 1>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b, M, n);
-        if (r != NORM_OK || !want) return r;
+        norm_status r = vec ? row_launch_bwd<T, RMS, VW>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b,
+                                                         dw_out, db_out, M, n)
+                            : row_launch_bwd<T, RMS, 1>(p, s, dy, x, w, mean, rstd, dx, part_w, part_b,
+                                                        dw_out, db_out, M, n);
+        if (r != NORM_OK || !want || direct) return r;
         row_launch_colsum<T>(s, part_w, part_b, p.grid, n, dw, db);
         return launch_status();
     });
