@@ -314,6 +314,10 @@ def measure(bench, steps, warmup, torch, hip, nl, flush):
             flush.add_(1)
             kev = [hip.event() for _ in range(2 * k)]
             nl.arm_kernel_events(kev)
+            # A stream event between the flush and the call, as in the span
+            # pass: without it the first kernel's start event was stamped
+            # ~2 us early (before the flush kernel had fully drained).
+            torch.cuda.Event().record()
             bench.run(op)
             names, main = nl.last_kernels()
             out[op] = (span, kev, names, main, h0, h1)
@@ -373,8 +377,10 @@ def summarize(bench, meas):
     names, main = meas["names"][bench.dominant]
     km = float(np.mean(meas["main"][bench.dominant]))
     kb = bench.bytes[bench.dominant + "_kernel"]
-    res["dominant_kernel"] = {"op": bench.dominant, "kernel": names[main] if main >= 0 else "",
-                              "avg_us": km * 1e3, "bytes": kb, "GBps": kb / km / 1e6}
+    kname = names[main] if main >= 0 else ""
+    res["dominant_kernel"] = {"op": bench.dominant, "kernel": kname, "avg_us": km * 1e3, "bytes": kb,
+                              "GBps": kb / km / 1e6,
+                              "traffic": load_traffic(f"{kname}|{wl.name}")}
     return res
 
 
