@@ -87,3 +87,21 @@ def test_backward_is_the_derivative(orc, act, param):
     f = lambda v: orc.act_dropout_fwd(v, act, 0.2, seed=123, offset=8, act_param=param)
     fd = dy * (f(x + h) - f(x - h)) / (2 * h)
     np.testing.assert_allclose(dx, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_mask_layout_known_answer(orc):
+    """Elements 0..3 under seed 0 use the four words of Philox4x32-10 at
+    counter 0 and key 0 -- the first published known-answer vector -- so
+    their keep flags at a set of thresholds are fixed by those words (a
+    different counter or word assignment changes the pattern)."""
+    kat = json.load(open(os.path.join(HERE, "golden", "philox4x32_10_kat.json")))["cases"][0]
+    assert kat["ctr"] == ["00000000"] * 4 and kat["key"] == ["00000000"] * 2
+    top = [int(v, 16) >> 8 for v in kat["out"]]
+    cuts = sorted(top)
+    # thresholds below, between and above the four 24-bit values
+    ts = [0, cuts[0] // 2] + [(a + b) // 2 for a, b in zip(cuts, cuts[1:])] + [cuts[-1] + 1]
+    for t in ts:
+        p = t / float(1 << 24)
+        assert orc.dropout_threshold(p) == t
+        expect = np.array([1 if v >= t else 0 for v in top], dtype=np.uint8)
+        np.testing.assert_array_equal(orc.dropout_keep(4, p, seed=0, offset=0), expect)
