@@ -300,30 +300,69 @@ template <int ACT, bool FAST = false> __device__ __forceinline__ float act_grad(
     } else return 1.0f;
 }
 
-// The rest of the family ([ActPage] section 6), evaluated in float32 with
-// the accurate device exp / tanh / log1p / expm1.  These share one kernel
-// instantiation per shape class and select the function with a wave-uniform
-// switch; definitions and the derivative conventions at kinks are
-// PyTorch's.  `p` is the leaky slope, or alpha of ELU / CELU.
+// The rest of the family ([ActPage] section 6), evaluated in float32.  These
+// share one kernel instantiation per shape class and select the function
+// with a wave-uniform switch; definitions and the derivative conventions at
+// kinks are PyTorch's.  `p` is the leaky slope, or alpha of ELU / CELU.
+// FAST = false uses the accurate device exp / tanh / log1p / expm1 and
+// IEEE division; FAST = true (16-bit outputs, as for GELU) builds them from
+// the hardware exp2 / log2 / reciprocal instructions: relative error a few
+// float32 ulps (1e-6 for |z| <= 20), or an absolute error near 1e-7 where a
+// result cancels towards 0 (tanh, expm1 and log1p of tiny arguments) --
+// far below a 16-bit ulp of the tensor's scale.
 constexpr float kSeluScale = 1.0507009873554804934f;
 constexpr float kSeluAlpha = 1.6732632423543772848f;
+constexpr float kLog2e = 1.4426950408889634074f;
+constexpr float kLn2 = 0.69314718055994530942f;
 
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
-__device__ __forceinline__ float softplus_f(float z) { return z > 20.0f ? z : log1pf(expf(z)); }
+template <bool FAST> __device__ __forceinline__ float exp_f(float z) {
+    if constexpr (FAST) return __builtin_amdgcn_exp2f(z * kLog2e);
+    else return expf(z);
+}
+template <bool FAST> __device__ __forceinline__ float expm1_f(float z) {
+    if constexpr (FAST) return __builtin_amdgcn_exp2f(z * kLog2e) - 1.0f;
+    else return expm1f(z);
+}
+template <bool FAST> __device__ __forceinline__ float recip_f(float v) {
+    if constexpr (FAST) return __builtin_amdgcn_rcpf(v);
+    else return 1.0f / v;
+}
+// log(1 + e^-|z|) for the softplus family: the argument lies in (0, 1].
+template <bool FAST> __device__ __forceinline__ float log1p_exp_neg_abs(float z) {
+    const float e = exp_f<FAST>(-fabsf(z));
+    if constexpr (FAST) return __builtin_amdgcn_logf(1.0f + e) * kLn2;
+    else return log1pf(e);
+}
+template <bool FAST> __device__ __forceinline__ float sigmoid_f(float z) {
+    return recip_f<FAST>(1.0f + exp_f<FAST>(-z));
+}
+template <bool FAST> __device__ __forceinline__ float tanh_f(float z) {
+    if constexpr (FAST) {
+        const float e = __builtin_amdgcn_exp2f(fabsf(z) * (-2.0f * kLog2e));
+        return copysignf((1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e), z);
+    } else {
+        return tanhf(z);
+    }
+}
+// softplus(z) = max(z, 0) + log(1 + e^-|z|), the identity above 20.
+template <bool FAST> __device__ __forceinline__ float softplus_f(float z) {
+    return z > 20.0f ? z : fmaxf(z, 0.0f) + log1p_exp_neg_abs<FAST>(z);
+}
 
+template <bool FAST = false>
 __device__ inline float act_fwd_rt(int act, float p, float z) {
     switch (act) {
     case kActRelu: return z > 0.0f ? z : 0.0f;
     case kActGelu: return 0.5f * z * (1.0f + erff(z * kInvSqrt2));
-    case kActSigmoid: return sigmoid_f(z);
-    case kActTanh: return tanhf(z);
-    case kActSilu: return z * sigmoid_f(z);
-    case kActMish: return z * tanhf(log1pf(expf(z)));
+    case kActSigmoid: return sigmoid_f<FAST>(z);
+    case kActTanh: return tanh_f<FAST>(z);
+    case kActSilu: return z * sigmoid_f<FAST>(z);
+    case kActMish: return z * tanh_f<FAST>(softplus_f<FAST>(z));
     case kActLeakyRelu: return z > 0.0f ? z : p * z;
-    case kActElu: return z > 0.0f ? z : p * expm1f(z);
-    case kActSelu: return kSeluScale * (z > 0.0f ? z : kSeluAlpha * expm1f(z));
-    case kActCelu: return z > 0.0f ? z : p * expm1f(z / p);
-    case kActSoftplus: return softplus_f(z);
+    case kActElu: return z > 0.0f ? z : p * expm1_f<FAST>(z);
+    case kActSelu: return kSeluScale * (z > 0.0f ? z : kSeluAlpha * expm1_f<FAST>(z));
+    case kActCelu: return z > 0.0f ? z : p * expm1_f<FAST>(z * recip_f<FAST>(p));
+    case kActSoftplus: return softplus_f<FAST>(z);
     case kActRelu6: return fminf(fmaxf(z, 0.0f), 6.0f);
     case kActHardsigmoid: return z <= -3.0f ? 0.0f : (z >= 3.0f ? 1.0f : z * (1.0f / 6.0f) + 0.5f);
     case kActHardswish: return z <= -3.0f ? 0.0f : (z >= 3.0f ? z : z * (z + 3.0f) * (1.0f / 6.0f));
@@ -331,22 +370,23 @@ __device__ inline float act_fwd_rt(int act, float p, float z) {
     }
 }
 
+template <bool FAST = false>
 __device__ inline float act_grad_rt(int act, float p, float z) {
     switch (act) {
     case kActRelu: return z > 0.0f ? 1.0f : 0.0f;
     case kActGelu: return act_grad<kActGelu, false>(z);
-    case kActSigmoid: { const float s = sigmoid_f(z); return s * (1.0f - s); }
-    case kActTanh: { const float t = tanhf(z); return 1.0f - t * t; }
-    case kActSilu: { const float s = sigmoid_f(z); return s * (1.0f + z * (1.0f - s)); }
+    case kActSigmoid: { const float s = sigmoid_f<FAST>(z); return s * (1.0f - s); }
+    case kActTanh: { const float t = tanh_f<FAST>(z); return 1.0f - t * t; }
+    case kActSilu: { const float s = sigmoid_f<FAST>(z); return s * (1.0f + z * (1.0f - s)); }
     case kActMish: {
-        const float t = tanhf(log1pf(expf(z)));
-        return t + z * sigmoid_f(z) * (1.0f - t * t);
+        const float t = tanh_f<FAST>(softplus_f<FAST>(z));
+        return t + z * sigmoid_f<FAST>(z) * (1.0f - t * t);
     }
     case kActLeakyRelu: return z > 0.0f ? 1.0f : p;
-    case kActElu: return z > 0.0f ? 1.0f : p * expf(z);
-    case kActSelu: return kSeluScale * (z > 0.0f ? 1.0f : kSeluAlpha * expf(z));
-    case kActCelu: return z > 0.0f ? 1.0f : expf(z / p);
-    case kActSoftplus: return z > 20.0f ? 1.0f : sigmoid_f(z);
+    case kActElu: return z > 0.0f ? 1.0f : p * exp_f<FAST>(z);
+    case kActSelu: return kSeluScale * (z > 0.0f ? 1.0f : kSeluAlpha * exp_f<FAST>(z));
+    case kActCelu: return z > 0.0f ? 1.0f : exp_f<FAST>(z * recip_f<FAST>(p));
+    case kActSoftplus: return z > 20.0f ? 1.0f : sigmoid_f<FAST>(z);
     case kActRelu6: return (z > 0.0f && z < 6.0f) ? 1.0f : 0.0f;
     case kActHardsigmoid: return (z > -3.0f && z < 3.0f) ? (1.0f / 6.0f) : 0.0f;
     case kActHardswish: return z <= -3.0f ? 0.0f : (z < 3.0f ? z * (1.0f / 3.0f) + 0.5f : 1.0f);
@@ -357,12 +397,12 @@ __device__ inline float act_grad_rt(int act, float p, float z) {
 // Compile-time activation, or the run-time one for ACT == kActGeneric.
 template <int ACT, bool FAST>
 __device__ __forceinline__ float act_fwd_any(float z, int act_rt, float p) {
-    if constexpr (ACT == kActGeneric) return act_fwd_rt(act_rt, p, z);
+    if constexpr (ACT == kActGeneric) return act_fwd_rt<FAST>(act_rt, p, z);
     else return act_fwd<ACT, FAST>(z);
 }
 template <int ACT, bool FAST>
 __device__ __forceinline__ float act_grad_any(float z, int act_rt, float p) {
-    if constexpr (ACT == kActGeneric) return act_grad_rt(act_rt, p, z);
+    if constexpr (ACT == kActGeneric) return act_grad_rt<FAST>(act_rt, p, z);
     else return act_grad<ACT, FAST>(z);
 }
 
