@@ -378,9 +378,10 @@ def summarize(bench, meas):
     km = float(np.mean(meas["main"][bench.dominant]))
     kb = bench.bytes[bench.dominant + "_kernel"]
     kname = names[main] if main >= 0 else ""
+    traffic = load_traffic(f"{kname}|{wl.name}")
     res["dominant_kernel"] = {"op": bench.dominant, "kernel": kname, "avg_us": km * 1e3, "bytes": kb,
-                              "GBps": kb / km / 1e6,
-                              "traffic": load_traffic(f"{kname}|{wl.name}")}
+                              "GBps": kb / km / 1e6, "traffic": traffic,
+                              "traffic_GBps": traffic / km / 1e6 if traffic else None}
     return res
 
 
