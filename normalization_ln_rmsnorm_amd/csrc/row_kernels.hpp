@@ -244,8 +244,13 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
 #pragma unroll
         for (int e = 0; e < V; ++e) acc_w[k][e] = acc_b[k][e] = 0.0f;
 
-    // Software pipelined: the next row's x, dy and statistics are loaded
-    // before this row is reduced and written.
+    // The next row's x, dy and statistics are issued before this row is
+    // reduced and written.  The loads sit under bounds branches, so the
+    // compiler waits for all outstanding loads before the first pass: in
+    // effect one row's reads are in flight per wave at a time.  Unconditional
+    // (clamped) loads that keep the next row in flight through the passes
+    // measured slower on the RMSNorm 16384 x 4096 backward: more reads in
+    // flight per CU lower this two-read, one-write pass's bandwidth.
     int slot = 0;
     const int64_t step = (int64_t)gridDim.x * rpb;
     int64_t base = (int64_t)blockIdx.x * rpb;

@@ -135,6 +135,34 @@ def test_unaligned_scalar_path(orc, kind):
     check(f"{kind} unaligned y", to_f64(y), ry, "f32")
 
 
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,ws_shift", [(1100, 130, 0), (2000, 256, 4), (777, 1003, 8)])
+def test_column_sum_paths(orc, kind, dtype, M, N, ws_shift):
+    """dw / db through the column-sum kernel: many partial rows, widths that
+    are not a multiple of 4 (scalar columns) and workspaces that are not
+    16-byte aligned (scalar loads), checked against the oracle."""
+    print(f"case colsum {kind} {dtype} {M}x{N} ws+{ws_shift}", flush=True)
+    wl = _wl(kind, dtype)
+    inp = gen_rowwise(wl, M=M, N=N)
+    bf16 = dtype == "bf16"
+    x, dy, w = (to_dev(inp[k], dtype) for k in ("x", "dy", "w"))
+    need = (nl.ln_bwd_workspace_bytes if kind == "ln" else nl.rms_bwd_workspace_bytes)(x.dtype, M, N)
+    big = torch.empty(need + 16, dtype=torch.uint8, device="cuda")
+    ws = big[ws_shift:ws_shift + need]
+    if kind == "ln":
+        b = to_dev(inp["b"], dtype)
+        _, mean, rstd = nl.ln_fwd(x, w, b, wl.eps)
+        _, dw, db = nl.ln_bwd(dy, x, w, mean, rstd, ws=ws)
+        _, rdw, rdb = orc.ln_bwd(inp["dy"], inp["x"], inp["w"], eps=wl.eps, bf16=bf16)
+        check(f"colsum {kind} db", to_f64(db), rdb, dtype)
+    else:
+        _, rstd = nl.rms_fwd(x, w, wl.eps)
+        _, dw = nl.rms_bwd(dy, x, w, rstd, ws=ws)
+        _, rdw = orc.rms_bwd(inp["dy"], inp["x"], inp["w"], eps=wl.eps, bf16=bf16)
+    check(f"colsum {kind} dw", to_f64(dw), rdw, dtype)
+
+
 @pytest.mark.parametrize("name", ["ln_f32_64x256", "rms_bf16_16384x4096", "ln_bf16_25216x768",
                                   "ln_bf16_4096x1000"])
 def test_full_size_workloads(orc, name):
