@@ -386,8 +386,9 @@ def summarize(bench, meas):
 
 
 def load_traffic(kernel_key):
-    """HBM traffic per launch recorded from rocprofv3 PMC runs, if the kernel
-    source still matches the one profiled (else None)."""
+    """HBM traffic per launch recorded from rocprofv3 PMC runs, if the
+    kernel's source files (its header and the shared headers it is compiled
+    from) still match the ones profiled (else None)."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.md")
     if not os.path.exists(path):
         return None
@@ -399,8 +400,11 @@ def load_traffic(kernel_key):
     rec = json.loads(m.group(1)).get(kernel_key)
     if not rec:
         return None
-    src = open(os.path.join(ROOT, rec["source"]), "rb").read()
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+    files = rec.get("sources")
+    if not files or not all(os.path.exists(os.path.join(ROOT, f)) for f in files):
+        return None  # a record this version cannot check
+    src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in files)
+    if hashlib.sha256(src).hexdigest() != rec.get("sources_sha256"):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -441,7 +445,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not "
-              "part of this build", file=sys.stderr)
+              "supported", file=sys.stderr)
         sys.exit(2)
     import torch
     import normalization_ln_rmsnorm_amd as nl

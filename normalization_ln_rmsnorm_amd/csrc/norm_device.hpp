@@ -240,48 +240,51 @@ constexpr float kInvSqrt2 = 0.70710678118654752440f;
 constexpr float kInvSqrt2Pi = 0.39894228040143267794f;
 constexpr float kNegHalfLog2e = -0.72134752044448170368f;  // -log2(e) / 2
 
-struct NormalPdfCdf {
-    float e;    // exp(-z^2 / 2)
-    float Phi;  // standard normal CDF at z
-};
+// Accurate GELU'(z) = Phi(z) + z phi(z) from the device erff and expf.
+__device__ __forceinline__ float gelu_grad_exact(float z) {
+    return fmaf(z * kInvSqrt2Pi, expf(-0.5f * z * z), 0.5f * (1.0f + erff(z * kInvSqrt2)));
+}
 
-template <bool FAST> __device__ __forceinline__ NormalPdfCdf normal_pdf_cdf(float z) {
-    if constexpr (FAST) {
-        const float e = __builtin_amdgcn_exp2f(z * z * kNegHalfLog2e);
-        const float u = fabsf(z) * kInvSqrt2;
-        const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, u, 1.0f));
-        float p = fmaf(t, 0.5307027145f, -0.7265760135f);
-        p = fmaf(t, p, 0.7107068705f);
-        p = fmaf(t, p, -0.142248368f);
-        p = fmaf(t, p, 0.127414796f);
-        const float q = p * t * e;  // Phi(-|z|)
-        return NormalPdfCdf{e, z >= 0.0f ? 1.0f - q : q};
-    } else {
-        return NormalPdfCdf{expf(-0.5f * z * z), 0.5f * (1.0f + erff(z * kInvSqrt2))};
-    }
+// Fast GELU'(z) (FAST = true).  With e = exp(-z^2 / 2) and Phi(-|z|) =
+// P(t) t e (the halved 7.1.26 polynomial P, t = 1 / (1 + p |z| / sqrt 2)):
+// Phi(z) = H(z) - s P(t) t e with H = 1, s = 1 for z >= 0 and H = 0, s = -1
+// below, so GELU'(z) = H + e (z / sqrt(2 pi) - s P(t) t): the sign, the two
+// products with e and the final add fold into two FMAs.
+__device__ __forceinline__ float gelu_grad_fast(float z) {
+    const float e = __builtin_amdgcn_exp2f(z * z * kNegHalfLog2e);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * kInvSqrt2, fabsf(z), 1.0f));
+    float p = fmaf(t, 0.5307027145f, -0.7265760135f);
+    p = fmaf(t, p, 0.7107068705f);
+    p = fmaf(t, p, -0.142248368f);
+    p = fmaf(t, p, 0.127414796f);
+    const bool pos = z >= 0.0f;
+    return fmaf(e, fmaf(pos ? -p : p, t, z * kInvSqrt2Pi), pos ? 1.0f : 0.0f);
 }
 
 // Fast forward GELU (FAST = true).  The forward needs Phi but not phi, so it
 // uses Abramowitz & Stegun eq. 7.1.28, erf(u) ~= 1 - 1 / (1 + a1 u + ... +
 // a6 u^6)^16 for u >= 0, |error| <= 3e-7, which costs one reciprocal and no
 // exp.  With r16 = (1 + a1 u + ... + a6 u^6)^-16 and u = |z| / sqrt 2,
-// z * Phi(z) = max(z, 0) - |z| * r16 / 2 for either sign of z.  In float32
+// z * Phi(z) = max(z, 0) - |z| * r16 / 2 for either sign of z.  The
+// polynomial is evaluated in |z| with every coefficient (the constant 1
+// included) scaled by 2^(1/16): a_i 2^(-i/2) 2^(1/16) for u^i, so its
+// reciprocal's 16th power is r16 / 2 and the result one FMA.  In float32
 // the result is within 7.1e-7 of GELU(z) (below 0.04 bf16 ulp wherever
 // |GELU(z)| > 2^-10).
 __device__ __forceinline__ float gelu_fast(float z) {
-    const float u = fabsf(z) * kInvSqrt2;
-    float p = fmaf(0.0000430638f, u, 0.0002765672f);
-    p = fmaf(p, u, 0.0001520143f);
-    p = fmaf(p, u, 0.0092705272f);
-    p = fmaf(p, u, 0.0422820123f);
-    p = fmaf(p, u, 0.0705230784f);
-    p = fmaf(p, u, 1.0f);
+    const float az = fabsf(z);
+    float p = fmaf(5.6212998e-06f, az, 5.1055209e-05f);
+    p = fmaf(p, az, 3.9686136e-05f);
+    p = fmaf(p, az, 3.4227392e-03f);
+    p = fmaf(p, az, 2.2076998e-02f);
+    p = fmaf(p, az, 5.2075163e-02f);
+    p = fmaf(p, az, 1.0442737f);  // 2^(1/16)
     float r = __builtin_amdgcn_rcpf(p);
     r *= r;
     r *= r;
     r *= r;
-    r *= r;  // r = p^-16
-    return fmaf(-0.5f * fabsf(z), r, fmaxf(z, 0.0f));
+    r *= r;  // r = p^-16 = r16 / 2
+    return fmaf(-az, r, fmaxf(z, 0.0f));
 }
 
 template <int ACT, bool FAST = false> __device__ __forceinline__ float act_fwd(float z) {
@@ -295,8 +298,8 @@ template <int ACT, bool FAST = false> __device__ __forceinline__ float act_fwd(f
 template <int ACT, bool FAST = false> __device__ __forceinline__ float act_grad(float z) {
     if constexpr (ACT == kActRelu) return z > 0.0f ? 1.0f : 0.0f;
     else if constexpr (ACT == kActGelu) {
-        const NormalPdfCdf n = normal_pdf_cdf<FAST>(z);
-        return fmaf(z * kInvSqrt2Pi, n.e, n.Phi);
+        if constexpr (FAST) return gelu_grad_fast(z);
+        else return gelu_grad_exact(z);
     } else return 1.0f;
 }
 
