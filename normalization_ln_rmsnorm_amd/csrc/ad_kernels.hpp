@@ -101,7 +101,6 @@ __device__ __forceinline__ void ad_fwd_range(const T *__restrict__ x, T *__restr
                                              int64_t v0, int64_t stride, const AdArgs &a) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
-    constexpr bool kFast = std::is_same<T, bf16_t>::value;
     for (int64_t vb = v0; vb < nvec; vb += stride * kAdUnroll) {
         raw_t r[kAdUnroll];
 #pragma unroll
@@ -119,7 +118,7 @@ __device__ __forceinline__ void ad_fwd_range(const T *__restrict__ x, T *__restr
                 if (DROP) keep_flags<V>(a, v, keep);
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    const float t = act_fwd_any<ACT, kFast>(f[e], a.act_rt, a.act_p);
+                    const float t = act_fwd_io<T, ACT>(f[e], a.act_rt, a.act_p);
                     o[e] = DROP ? (keep[e] ? t * a.scale : 0.0f) : t;
                 }
                 vstore_stream<T, V>(y + v * V, VT::pack(o));

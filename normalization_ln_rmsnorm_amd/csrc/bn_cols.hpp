@@ -198,7 +198,6 @@ bn_col_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T 
                     int act_rt, float act_p) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
-    constexpr bool kFast = std::is_same<T, bf16_t>::value;  // fp16 keeps the exact forms
     const ColPos p = col_pos(g, V);
     if (!p.active) return;  // no barriers in this kernel
     float a[V], s[V];
@@ -231,7 +230,7 @@ bn_col_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T 
                 for (int e = 0; e < V; ++e) {
                     float z = fmaf(f[e], a[e], s[e]);
                     if (RES) z += rf[e];
-                    o[e] = act_fwd_any<ACT, kFast>(z, act_rt, act_p);
+                    o[e] = act_fwd_io<T, ACT>(z, act_rt, act_p);
                 }
                 vstore_stream<T, V>(y + row * g.K + p.col0, VT::pack(o));
             }

@@ -168,7 +168,6 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
                 BnGeom g, int act_rt, float act_p) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
-    constexpr bool kFast = std::is_same<T, bf16_t>::value;  // fp16 keeps the exact forms
     int c; int64_t n0, n1;
     tile_of_block(g, &c, &n0, &n1);
     float mean, rstd;
@@ -209,7 +208,7 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
                     for (int e = 0; e < V; ++e) {
                         float z = fmaf(f[e], a, s);
                         if (RES) z += rf[e];
-                        o[e] = act_fwd_any<ACT, kFast>(z, act_rt, act_p);
+                        o[e] = act_fwd_io<T, ACT>(z, act_rt, act_p);
                     }
                     vstore_stream<T, V>(y + off + v * V, VT::pack(o));
                 }

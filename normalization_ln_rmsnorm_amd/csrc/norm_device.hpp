@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mi355norm {
 
 constexpr int kWave = 64;
@@ -287,6 +289,32 @@ __device__ __forceinline__ float gelu_fast(float z) {
     return fmaf(-az, r, fmaxf(z, 0.0f));
 }
 
+// GELU with a small relative error everywhere, the forward for fp16 I/O:
+// fp16 results reach 2^-24 in the negative tail, where the absolute error of
+// eq. 7.1.28 above is several fp16 ulps.  Press et al., Numerical Recipes
+// (2nd ed., section 6.2), give a Chebyshev fit erfc(u) ~= t exp(-u^2 -
+// 1.26551223 + t (1.00002368 + t (0.37409196 + ... + t 0.17087277))), t =
+// 1 / (1 + u / 2), with fractional error below 1.2e-7 for u >= 0.  With
+// u = |z| / sqrt 2, z Phi(z) = max(z, 0) - |z| erfc(u) / 2; log2(e) is folded
+// into the exponent's coefficients and the 1/2 into its constant (-1), so the
+// exponential is one exp2.  In float32 the result is within 0.003 fp16 ulp
+// wherever it is a normal fp16 (checked against float64 over |z| <= 16).
+__device__ __forceinline__ float gelu_fast_rel(float z) {
+    const float az = fabsf(z);
+    const float t = __builtin_amdgcn_rcpf(fmaf(az, 3.535533845e-01f, 1.0f));  // 1 / (1 + u / 2)
+    float p = fmaf(t, 2.465173006e-01f, -1.186114907e+00f);
+    p = fmaf(t, p, 2.147474527e+00f);
+    p = fmaf(t, p, -1.637753129e+00f);
+    p = fmaf(t, p, 4.023215771e-01f);
+    p = fmaf(t, p, -2.687568665e-01f);
+    p = fmaf(t, p, 1.396300495e-01f);
+    p = fmaf(t, p, 5.397006273e-01f);
+    p = fmaf(t, p, 1.442729235e+00f);
+    const float arg = fmaf(t, p, fmaf(z, z * -7.213475108e-01f, -2.825748205e+00f));
+    const float h = t * __builtin_amdgcn_exp2f(arg);  // erfc(u) / 2
+    return fmaf(-az, h, fmaxf(z, 0.0f));
+}
+
 template <int ACT, bool FAST = false> __device__ __forceinline__ float act_fwd(float z) {
     if constexpr (ACT == kActRelu) return z > 0.0f ? z : 0.0f;
     else if constexpr (ACT == kActGelu) {
@@ -402,6 +430,14 @@ template <int ACT, bool FAST>
 __device__ __forceinline__ float act_fwd_any(float z, int act_rt, float p) {
     if constexpr (ACT == kActGeneric) return act_fwd_rt<FAST>(act_rt, p, z);
     else return act_fwd<ACT, FAST>(z);
+}
+// Forward activation for I/O type T: bf16 takes the fast forms; fp16 the
+// exact ones, except GELU, which takes gelu_fast_rel; float32 the exact ones.
+template <typename T, int ACT>
+__device__ __forceinline__ float act_fwd_io(float z, int act_rt, float p) {
+    if constexpr (std::is_same<T, bf16_t>::value) return act_fwd_any<ACT, true>(z, act_rt, p);
+    else if constexpr (std::is_same<T, f16_t>::value && ACT == kActGelu) return gelu_fast_rel(z);
+    else return act_fwd_any<ACT, false>(z, act_rt, p);
 }
 template <int ACT, bool FAST>
 __device__ __forceinline__ float act_grad_any(float z, int act_rt, float p) {

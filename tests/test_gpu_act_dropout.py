@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests._parity import check, to_dev, to_f64
+from tests._parity import check, to_dev, to_f64, to_io
 
 pytestmark = pytest.mark.gpu
 
@@ -122,3 +122,45 @@ def test_full_size_workload(orc):
     nz = orc.widen(inp["x"], bf16=True) != 0
     assert (yv[keep == 0] == 0).all()
     assert np.array_equal((yv[nz] != 0).astype(np.uint8), keep[nz])
+
+
+TAIL_ACTS = [("gelu", 0.0), ("silu", 0.0), ("sigmoid", 0.0), ("tanh", 0.0), ("mish", 0.0),
+             ("softplus", 0.0), ("elu", 1.0), ("selu", 0.0), ("celu", 1.3)]
+
+
+def _grid(dtype, n=65536 + 5, lim=12.0):
+    return to_io(np.linspace(-lim, lim, n, dtype=np.float32), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("act,param", TAIL_ACTS)
+def test_activation_over_both_tails(orc, dtype, act, param):
+    """p = 0 (no dropout): the activation and its derivative on a dense grid
+    over [-12, 12] -- far into both tails, where the 16-bit forms differ most
+    from the exact ones -- element by element against the oracle (the
+    pre-activation is x itself, so the kinks of elu / selu at 0 are decided
+    on the same value on both sides)."""
+    print(f"case tails {dtype} {act}", flush=True)
+    bf16 = dtype == "bf16"
+    xs = _grid(dtype)
+    ones = to_io(np.ones(xs.shape[0], dtype=np.float32), dtype)
+    x, dy = to_dev(xs, dtype), to_dev(ones, dtype)
+    y = nl.act_dropout_fwd(x, act, 0.0, 5, 0, act_param=param)
+    dx = nl.act_dropout_bwd(dy, x, act, 0.0, 5, 0, act_param=param)
+    torch.cuda.synchronize()
+    check(f"tails {dtype} {act} y", to_f64(y), orc.act_dropout_fwd(xs, act, 0.0, 5, 0, act_param=param, bf16=bf16),
+          dtype)
+    check(f"tails {dtype} {act} dx", to_f64(dx),
+          orc.act_dropout_bwd(ones, xs, act, 0.0, 5, 0, act_param=param, bf16=bf16), dtype)
+
+
+def test_fp16_gelu_forward_tail_is_relatively_accurate(orc):
+    """The fp16 GELU forward keeps a small relative error in its negative
+    tail (results down to fp16's subnormals): checked with the tolerance floor
+    taken over each run of 64 neighbouring grid points, so every value is
+    held to about 2 ulp of its own magnitude."""
+    xs = _grid("f16", n=64 * 2048)
+    y = nl.act_dropout_fwd(to_dev(xs, "f16"), "gelu", 0.0, 5, 0)
+    torch.cuda.synchronize()
+    ref = orc.act_dropout_fwd(xs, "gelu", 0.0, 5, 0)
+    check("fp16 gelu tail y", to_f64(y).reshape(-1, 64), ref.reshape(-1, 64), "f16", group_axis=1)
