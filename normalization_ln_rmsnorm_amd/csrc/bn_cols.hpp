@@ -254,6 +254,7 @@ bn_col_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, cons
     using raw_t = typename VT::raw_t;
     constexpr bool kExact = sizeof(T) == 4;
     constexpr bool kFast = kFastGrad<T>;
+    constexpr bool kPre = kGeluPrescale<T, ACT, RES>;
     constexpr int NS = kExact ? 3 : 2;
     using Acc = typename std::conditional<kExact, double, float>::type;
     const ColPos p = col_pos(g, V);
@@ -270,6 +271,10 @@ bn_col_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, cons
             const int64_t c = (p.col0 + e) / g.HW;
             mean[e] = save_mean[c];
             bn_coeffs(mean[e], save_rstd[c], w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a[e], &s[e]);
+            if (kPre) {
+                a[e] *= kGeluWScale;
+                s[e] *= kGeluWScale;
+            }
         }
         const int64_t step = (int64_t)g.RPP;
         for (int64_t r = p.r0 + p.rs; r < p.r1; r += step * kBnUnroll) {
@@ -297,7 +302,7 @@ bn_col_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, cons
                         if (ACT != kActNone) {
                             float z = fmaf(xf[e], a[e], s[e]);
                             if (RES) z += rf[e];
-                            dz[e] = df[e] * act_grad_any<ACT, kFast>(z, act_rt, act_p);
+                            dz[e] = df[e] * (kPre ? gelu_grad_fast_w(z) : act_grad_any<ACT, kFast>(z, act_rt, act_p));
                         } else {
                             dz[e] = df[e];
                         }
@@ -407,6 +412,7 @@ bn_col_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
     using raw_t = typename VT::raw_t;
     constexpr bool kExact = sizeof(T) == 4;
     constexpr bool kFast = kFastGrad<T>;
+    constexpr bool kPre = kGeluPrescale<T, ACT, RES>;
     const ColPos p = col_pos(g, V);
     if (!p.active) return;  // no barriers in this kernel
     float k1[V], k2[V], k3[V], mean[V], a[V], s[V];
@@ -420,6 +426,10 @@ bn_col_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
         a[e] = s[e] = 0.0f;
         if (DZ_SRC == 2)
             bn_coeffs(mean[e], save_rstd[c], w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a[e], &s[e]);
+        if (kPre) {
+            a[e] *= kGeluWScale;
+            s[e] *= kGeluWScale;
+        }
     }
     const T *dzsrc = DZ_SRC == 1 ? dres : dy;
     const int64_t step = (int64_t)g.RPP;
@@ -449,7 +459,7 @@ bn_col_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
                     if (DZ_SRC == 2 && ACT != kActNone) {
                         float z = fmaf(xf[e], a[e], s[e]);
                         if (RES) z += rf[e];
-                        dz = df[e] * act_grad_any<ACT, kFast>(z, act_rt, act_p);
+                        dz = df[e] * (kPre ? gelu_grad_fast_w(z) : act_grad_any<ACT, kFast>(z, act_rt, act_p));
                     }
                     o[e] = kExact ? fmaf(k1[e], dz, fmaf(k2[e], xf[e] - mean[e], k3[e]))
                                   : fmaf(k1[e], dz, fmaf(k2[e], xf[e], k3[e]));

@@ -35,6 +35,13 @@ constexpr int kBnUnroll = 4;             // vectors in flight per thread per ste
 template <typename T>
 constexpr bool kFastGrad = sizeof(T) == 2;
 
+// The backward passes of a GELU without a residual, for 16-bit I/O, scale
+// the per-channel a, s by kGeluWScale and evaluate gelu_grad_fast_w on
+// x a + s (with a residual, z = x a + s + res would need res scaled too).
+template <typename T, int ACT, bool RES>
+constexpr bool kGeluPrescale = ACT == kActGelu && kFastGrad<T> && !RES;
+
+
 // Per-channel scale and shift shared by the forward apply and the backward
 // recompute, so both evaluate z with identical float32 operations.
 __device__ __forceinline__ void bn_coeffs(float mean, float rstd, float w, float b, float *a, float *s) {

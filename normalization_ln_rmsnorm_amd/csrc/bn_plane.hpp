@@ -232,6 +232,11 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
     const float mean = save_mean[c];
     float a, s;
     bn_coeffs(mean, save_rstd[c], w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a, &s);
+    constexpr bool kPre = kGeluPrescale<T, ACT, RES>;
+    if (kPre) {
+        a *= kGeluWScale;
+        s *= kGeluWScale;
+    }
     const int64_t nvp = g.HW / V;
 
     // Accumulation.  Float32 I/O: float64 per element, so x - mean and
@@ -272,7 +277,8 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
                         if (ACT != kActNone) {
                             float z = fmaf(xf[e], a, s);
                             if (RES) z += rf[e];
-                            dz[e] = df[e] * act_grad_any<ACT, kFastGrad<T>>(z, act_rt, act_p);
+                            dz[e] = df[e] * (kPre ? gelu_grad_fast_w(z)
+                                                  : act_grad_any<ACT, kFastGrad<T>>(z, act_rt, act_p));
                         } else {
                             dz[e] = df[e];
                         }
@@ -376,6 +382,11 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
     const float k3m = kc.k3m;
     float a = 0.0f, s = 0.0f;
     if (DZ_SRC == 2) bn_coeffs(mean, rstd_f, wc_f, b ? ld1(b + c) : 0.0f, &a, &s);
+    constexpr bool kPre = kGeluPrescale<T, ACT, RES>;
+    if (kPre) {
+        a *= kGeluWScale;
+        s *= kGeluWScale;
+    }
     const int64_t nvp = g.HW / V;
     const T *dzsrc = DZ_SRC == 1 ? dres : dy;
 
@@ -406,7 +417,7 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
                         if (DZ_SRC == 2 && ACT != kActNone) {
                             float z = fmaf(xf[e], a, s);
                             if (RES) z += rf[e];
-                            dz = df[e] * act_grad_any<ACT, kFast>(z, act_rt, act_p);
+                            dz = df[e] * (kPre ? gelu_grad_fast_w(z) : act_grad_any<ACT, kFast>(z, act_rt, act_p));
                         }
                         o[e] = kExact ? fmaf(k1, dz, fmaf(k2, xf[e] - mean, k3)) : fmaf(k1, dz, fmaf(k2, xf[e], k3m));
                     }

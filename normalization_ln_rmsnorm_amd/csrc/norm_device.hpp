@@ -263,6 +263,22 @@ __device__ __forceinline__ float gelu_grad_fast(float z) {
     return fmaf(e, fmaf(pos ? -p : p, t, z * kInvSqrt2Pi), pos ? 1.0f : 0.0f);
 }
 
+// gelu_grad_fast of z = w / kGeluWScale.  A caller that forms z as x a + s
+// can scale a and s by kGeluWScale = sqrt(log2(e) / 2) once and pass w: the
+// exp2 argument -z^2 log2(e) / 2 is then -w^2, one multiply per element
+// fewer; the other constants absorb 1 / kGeluWScale.  Same error bound.
+constexpr float kGeluWScale = 0.84932180f;
+__device__ __forceinline__ float gelu_grad_fast_w(float w) {
+    const float e = __builtin_amdgcn_exp2f(-w * w);
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.27273747f, fabsf(w), 1.0f));  // p / sqrt 2 / kGeluWScale
+    float p = fmaf(t, 0.5307027145f, -0.7265760135f);
+    p = fmaf(t, p, 0.7107068705f);
+    p = fmaf(t, p, -0.142248368f);
+    p = fmaf(t, p, 0.127414796f);
+    const bool pos = w >= 0.0f;
+    return fmaf(e, fmaf(pos ? -p : p, t, w * 0.46971864f), pos ? 1.0f : 0.0f);  // 1 / sqrt(2 pi) / kGeluWScale
+}
+
 // Fast forward GELU (FAST = true).  The forward needs Phi but not phi, so it
 // uses Abramowitz & Stegun eq. 7.1.28, erf(u) ~= 1 - 1 / (1 + a1 u + ... +
 // a6 u^6)^16 for u >= 0, |error| <= 3e-7, which costs one reciprocal and no
