@@ -33,6 +33,9 @@
  *   workspace; the library never allocates, frees or synchronizes, and keeps
  *   no state between calls.  Concurrent calls are safe if they use distinct
  *   output and workspace buffers.  Outputs must not alias inputs.
+ * Capture.  A call enqueues kernels only (no memset, copy or host wait), so
+ *   it can be recorded into a HIP graph by stream capture and replayed; the
+ *   pointers and sizes are fixed at capture, as for any captured launch.
  * Errors.  Every entry point returns a norm_status.  Arguments are checked
  *   on the host before anything is enqueued; on an error nothing is
  *   launched and no output is touched.  A zero-sized problem (M == 0, or
