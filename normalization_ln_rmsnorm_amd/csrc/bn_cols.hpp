@@ -50,10 +50,23 @@ struct ColPos {
     bool active;     // lane maps to a real vector of a real slice
 };
 
+// Workgroups are dispatched to the chip's 8 XCDs round-robin by index, and
+// each XCD has its own L2.  The swizzle gives the column chunks of one row
+// tile consecutive slots on one XCD, so the rows they share are read through
+// one L2 in a short window rather than as 1 KiB slices by every XCD.  A
+// bijection on [0, G) for any G (the first G mod 8 XCDs take one more).
+constexpr int kXcds = 8;
+__device__ __forceinline__ unsigned xcd_swizzle(unsigned b, unsigned G) {
+    const unsigned q = G / kXcds, r = G % kXcds;
+    const unsigned x = b % kXcds, j = b / kXcds;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+}
+
 __device__ __forceinline__ ColPos col_pos(const BnColGeom &g, int V) {
     ColPos p;
-    const int chunk = (int)(blockIdx.x % (unsigned)g.NCH);
-    p.tile = (int)(blockIdx.x / (unsigned)g.NCH);
+    const unsigned id = xcd_swizzle(blockIdx.x, gridDim.x);
+    const int chunk = (int)(id % (unsigned)g.NCH);
+    p.tile = (int)(id / (unsigned)g.NCH);
     const int cv = (int)(threadIdx.x % (unsigned)g.CV);
     p.rs = (int)(threadIdx.x / (unsigned)g.CV);
     const int64_t vi = (int64_t)chunk * g.CV + cv;
