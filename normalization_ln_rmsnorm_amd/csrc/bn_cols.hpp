@@ -50,18 +50,9 @@ struct ColPos {
     bool active;     // lane maps to a real vector of a real slice
 };
 
-// Workgroups are dispatched to the chip's 8 XCDs round-robin by index, and
-// each XCD has its own L2.  The swizzle gives the column chunks of one row
-// tile consecutive slots on one XCD, so the rows they share are read through
-// one L2 in a short window rather than as 1 KiB slices by every XCD.  A
-// bijection on [0, G) for any G (the first G mod 8 XCDs take one more).
-constexpr int kXcds = 8;
-__device__ __forceinline__ unsigned xcd_swizzle(unsigned b, unsigned G) {
-    const unsigned q = G / kXcds, r = G % kXcds;
-    const unsigned x = b % kXcds, j = b / kXcds;
-    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
-}
-
+// The column chunks of one row tile take consecutive slots on one XCD
+// (xcd_swizzle), so the rows they share are read through one L2 in a short
+// window rather than as 1 KiB slices by every XCD.
 __device__ __forceinline__ ColPos col_pos(const BnColGeom &g, int V) {
     ColPos p;
     const unsigned id = xcd_swizzle(blockIdx.x, gridDim.x);

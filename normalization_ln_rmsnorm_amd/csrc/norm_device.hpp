@@ -210,6 +210,18 @@ __device__ __forceinline__ double shfl_xor_d(double v, int mask) {
     return __shfl_xor(v, mask, kWave);
 }
 
+// Workgroups are dispatched to the chip's 8 XCDs round-robin by linear
+// index, and each XCD has its own L2.  xcd_swizzle maps dispatch index b to
+// a logical index such that consecutive logical indices run on the same XCD:
+// XCD x takes a contiguous range of them.  A bijection on [0, G) for any G
+// (the first G mod 8 XCDs take one more).
+constexpr unsigned kXcds = 8;
+__device__ __forceinline__ unsigned xcd_swizzle(unsigned b, unsigned G) {
+    const unsigned q = G / kXcds, r = G % kXcds;
+    const unsigned x = b % kXcds, j = b / kXcds;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+}
+
 // ------------------------------------------------------------ activations
 // ReLU and the exact error-function GELU ([ActPage] sections 5-6), computed
 // in float32.  GELU(z) = z * Phi(z), Phi(z) = (1 + erf(z / sqrt 2)) / 2;
