@@ -120,8 +120,10 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
         }
     }
 
-    // Software pipelined: the next row's loads are issued before this row is
-    // reduced and stored, so every wave keeps loads in flight.
+    // Row loop (one pass per block on the default, non-persistent grid; more
+    // on a persistent grid).  The next row's loads are issued before this
+    // row is reduced and stored; they sit under bounds branches, so the
+    // compiler waits for all outstanding loads before the row's first pass.
     const int64_t step = (int64_t)gridDim.x * rpb;
     int64_t base = (int64_t)blockIdx.x * rpb;
     raw_t xr[IT];
