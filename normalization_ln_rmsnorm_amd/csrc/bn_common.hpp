@@ -26,7 +26,13 @@ namespace mi355norm {
 
 constexpr int kBnBlock = 256;
 constexpr int kBnWaves = kBnBlock / kWave;
-constexpr int kBnUnroll = 4;             // vectors in flight per thread per step
+constexpr int kBnUnroll = 4;             // vectors in flight per thread per step: statistics,
+                                         // backward reduction and the column path
+constexpr int kBnUnrollStream = 8;       // the same for the plane apply and dx passes, which
+                                         // stream with little arithmetic (measured: 4 -> 8 took
+                                         // the bf16 GELU dx pass 204.6 -> 199.8 us and apply
+                                         // 143.9 -> 141.0 us; the VALU-bound reduction, 143 ->
+                                         // 147 us, keeps 4)
 
 // Which activations take the fast (published-approximation) forms of GELU:
 // the forward only for bf16 (fp16's 11-bit significand resolves the

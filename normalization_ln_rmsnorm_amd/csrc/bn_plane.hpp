@@ -187,10 +187,10 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
 
     for (int64_t n = n0; n < n1; ++n) {
         const int64_t off = plane_offset(g, n, c);
-        for (int64_t v0 = threadIdx.x; v0 < nvp; v0 += (int64_t)kBnBlock * kBnUnroll) {
-            raw_t rx[kBnUnroll], rr[kBnUnroll];
+        for (int64_t v0 = threadIdx.x; v0 < nvp; v0 += (int64_t)kBnBlock * kBnUnrollStream) {
+            raw_t rx[kBnUnrollStream], rr[kBnUnrollStream];
 #pragma unroll
-            for (int u = 0; u < kBnUnroll; ++u) {
+            for (int u = 0; u < kBnUnrollStream; ++u) {
                 const int64_t v = v0 + (int64_t)u * kBnBlock;
                 if (v < nvp) {
                     rx[u] = vload_stream<T, V>(x + off + v * V);
@@ -198,7 +198,7 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
                 }
             }
 #pragma unroll
-            for (int u = 0; u < kBnUnroll; ++u) {
+            for (int u = 0; u < kBnUnrollStream; ++u) {
                 const int64_t v = v0 + (int64_t)u * kBnBlock;
                 if (v < nvp) {
                     float f[V], rf[V], o[V];
@@ -392,10 +392,10 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
 
     for (int64_t n = n0; n < n1; ++n) {
         const int64_t off = plane_offset(g, n, c);
-        for (int64_t v0 = threadIdx.x; v0 < nvp; v0 += (int64_t)kBnBlock * kBnUnroll) {
-            raw_t rd[kBnUnroll], rx[kBnUnroll], rr[kBnUnroll];
+        for (int64_t v0 = threadIdx.x; v0 < nvp; v0 += (int64_t)kBnBlock * kBnUnrollStream) {
+            raw_t rd[kBnUnrollStream], rx[kBnUnrollStream], rr[kBnUnrollStream];
 #pragma unroll
-            for (int u = 0; u < kBnUnroll; ++u) {
+            for (int u = 0; u < kBnUnrollStream; ++u) {
                 const int64_t v = v0 + (int64_t)u * kBnBlock;
                 if (v < nvp) {
                     rd[u] = vload_stream<T, V>(dzsrc + off + v * V);
@@ -404,7 +404,7 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
                 }
             }
 #pragma unroll
-            for (int u = 0; u < kBnUnroll; ++u) {
+            for (int u = 0; u < kBnUnrollStream; ++u) {
                 const int64_t v = v0 + (int64_t)u * kBnBlock;
                 if (v < nvp) {
                     float df[V], xf[V], rf[V], o[V];
