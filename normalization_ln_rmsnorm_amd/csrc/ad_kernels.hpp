@@ -95,10 +95,12 @@ __device__ __forceinline__ void keep_flags(const AdArgs &a, int64_t vi, bool kee
 
 // Forward over vectors v0, v0 + stride, ... below nvec, kAdUnroll loads in
 // flight (vector v holds elements v * V .. v * V + V - 1).  DROP = false is
-// the plain activation (p = 0: no generator calls).
+// the plain activation (p = 0: no generator calls).  `ub` is a vector index
+// at or below v0 that is the same in every lane (the range's first vector);
+// outputs are stored relative to it.
 template <typename T, int V, int ACT, bool DROP>
 __device__ __forceinline__ void ad_fwd_range(const T *__restrict__ x, T *__restrict__ y, int64_t nvec,
-                                             int64_t v0, int64_t stride, const AdArgs &a) {
+                                             int64_t v0, int64_t stride, int64_t ub, const AdArgs &a) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
     for (int64_t vb = v0; vb < nvec; vb += stride * kAdUnroll) {
@@ -121,7 +123,7 @@ __device__ __forceinline__ void ad_fwd_range(const T *__restrict__ x, T *__restr
                     const float t = act_fwd_io<T, ACT>(f[e], a.act_rt, a.act_p);
                     o[e] = DROP ? (keep[e] ? t * a.scale : 0.0f) : t;
                 }
-                vstore_stream<T, V>(y + v * V, VT::pack(o));
+                vstore_out<T, V>(y + ub * V, (uint32_t)((v - ub) * V), VT::pack(o));
             }
         }
     }
@@ -130,7 +132,7 @@ __device__ __forceinline__ void ad_fwd_range(const T *__restrict__ x, T *__restr
 template <typename T, int V, int ACT, bool DROP>
 __device__ __forceinline__ void ad_bwd_range(const T *__restrict__ dy, const T *__restrict__ x,
                                              T *__restrict__ dx, int64_t nvec, int64_t v0, int64_t stride,
-                                             const AdArgs &a) {
+                                             int64_t ub, const AdArgs &a) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
     constexpr bool kFast = sizeof(T) == 2;
@@ -158,7 +160,7 @@ __device__ __forceinline__ void ad_bwd_range(const T *__restrict__ dy, const T *
                     const float g = df[e] * act_grad_any<ACT, kFast>(xf[e], a.act_rt, a.act_p);
                     o[e] = DROP ? (keep[e] ? g * a.scale : 0.0f) : g;
                 }
-                vstore_stream<T, V>(dx + v * V, VT::pack(o));
+                vstore_out<T, V>(dx + ub * V, (uint32_t)((v - ub) * V), VT::pack(o));
             }
         }
     }
@@ -175,12 +177,12 @@ act_dropout_fwd_kernel(const T *__restrict__ x, T *__restrict__ y, AdArgs a) {
     // Each block covers kAdUnroll * kAdBlock consecutive vectors per pass.
     for (int64_t base = (int64_t)blockIdx.x * kAdBlock * kAdUnroll; base < nvec; base += stride)
         ad_fwd_range<T, V, ACT, DROP>(x, y, base + kAdBlock * kAdUnroll < nvec ? base + kAdBlock * kAdUnroll : nvec,
-                                      base + threadIdx.x, kAdBlock, a);
+                                      base + threadIdx.x, kAdBlock, base, a);
     if (V > 1) {
         const int64_t tail = a.n - nvec * V;
         if (t0 < tail) {
             const int64_t i = nvec * V + t0;
-            ad_fwd_range<T, 1, ACT, DROP>(x, y, i + 1, i, 1, a);
+            ad_fwd_range<T, 1, ACT, DROP>(x, y, i + 1, i, 1, nvec * V, a);
         }
     }
 }
@@ -193,12 +195,12 @@ act_dropout_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__r
     const int64_t stride = (int64_t)gridDim.x * kAdBlock * kAdUnroll;
     for (int64_t base = (int64_t)blockIdx.x * kAdBlock * kAdUnroll; base < nvec; base += stride)
         ad_bwd_range<T, V, ACT, DROP>(dy, x, dx, base + kAdBlock * kAdUnroll < nvec ? base + kAdBlock * kAdUnroll : nvec,
-                                      base + threadIdx.x, kAdBlock, a);
+                                      base + threadIdx.x, kAdBlock, base, a);
     if (V > 1) {
         const int64_t tail = a.n - nvec * V;
         if (t0 < tail) {
             const int64_t i = nvec * V + t0;
-            ad_bwd_range<T, 1, ACT, DROP>(dy, x, dx, i + 1, i, 1, a);
+            ad_bwd_range<T, 1, ACT, DROP>(dy, x, dx, i + 1, i, 1, nvec * V, a);
         }
     }
 }

@@ -44,6 +44,7 @@ namespace mi355norm {
 // Position of this thread in the column geometry.
 struct ColPos {
     int64_t col0;    // first of the thread's V columns
+    int64_t cb;      // first column of the block's chunk (the same in every lane)
     int64_t r0, r1;  // the tile's rows [r0, r1)
     int rs;          // row slice: rows r0 + rs, r0 + rs + RPP, ...
     int tile;
@@ -63,10 +64,28 @@ __device__ __forceinline__ ColPos col_pos(const BnColGeom &g, int V) {
     const int64_t vi = (int64_t)chunk * g.CV + cv;
     p.active = p.rs < g.RPP && vi < g.KV;
     p.col0 = vi * V;
+    p.cb = (int64_t)chunk * g.CV * V;
     p.r0 = (int64_t)p.tile * g.RT;
     const int64_t e = p.r0 + g.RT;
     p.r1 = e < g.Nb ? e : g.Nb;
     return p;
+}
+
+// Output store of the thread's vector in row `row`.  When the block's tile
+// spans under 4 GiB it is addressed from the tile's first row and the
+// chunk's first column (the same in every lane) and written with the
+// device-scope buffer store; otherwise with a non-temporal global store.
+template <typename T>
+__device__ __forceinline__ bool col_sc1_ok(const BnColGeom &g) {
+    return (int64_t)g.RT * g.K * (int64_t)sizeof(T) <= (int64_t)0xffffffff;
+}
+template <typename T, int V>
+__device__ __forceinline__ void col_store(T *out, const BnColGeom &g, const ColPos &p, int64_t row,
+                                          const typename Vec<T, V>::raw_t &r, bool sc1_ok) {
+    if (sc1_ok)
+        vstore_out<T, V>(out + p.r0 * g.K + p.cb, (uint32_t)((row - p.r0) * g.K + (p.col0 - p.cb)), r);
+    else
+        vstore_stream<T, V>(out + row * g.K + p.col0, r);
 }
 
 __device__ __forceinline__ int tree_start(int rpp) {
@@ -203,6 +222,7 @@ bn_col_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T 
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
     const ColPos p = col_pos(g, V);
+    const bool sc1_ok = col_sc1_ok<T>(g);
     if (!p.active) return;  // no barriers in this kernel
     float a[V], s[V];
 #pragma unroll
@@ -236,7 +256,7 @@ bn_col_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T 
                     if (RES) z += rf[e];
                     o[e] = act_fwd_io<T, ACT>(z, act_rt, act_p);
                 }
-                vstore_stream<T, V>(y + row * g.K + p.col0, VT::pack(o));
+                col_store<T, V>(y, g, p, row, VT::pack(o), sc1_ok);
             }
         }
     }
@@ -262,6 +282,7 @@ bn_col_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, cons
     constexpr int NS = kExact ? 3 : 2;
     using Acc = typename std::conditional<kExact, double, float>::type;
     const ColPos p = col_pos(g, V);
+    const bool sc1_ok = col_sc1_ok<T>(g);
     Acc s_dz[V], s_dzx[V], s_xc[V];
     float a[V], s[V], mean[V];
 #pragma unroll
@@ -316,7 +337,7 @@ bn_col_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, cons
                         s_dzx[e] = fma(d, xc, s_dzx[e]);
                         if (kExact) s_xc[e] += xc;
                     }
-                    if (RES) vstore_stream<T, V>(dres + row * g.K + p.col0, VT::pack(dz));
+                    if (RES) col_store<T, V>(dres, g, p, row, VT::pack(dz), sc1_ok);
                 }
             }
         }
@@ -418,6 +439,7 @@ bn_col_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
     constexpr bool kFast = kFastGrad<T>;
     constexpr bool kPre = kGeluPrescale<T, ACT, RES>;
     const ColPos p = col_pos(g, V);
+    const bool sc1_ok = col_sc1_ok<T>(g);
     if (!p.active) return;  // no barriers in this kernel
     float k1[V], k2[V], k3[V], mean[V], a[V], s[V];
 #pragma unroll
@@ -468,7 +490,7 @@ bn_col_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
                     o[e] = kExact ? fmaf(k1[e], dz, fmaf(k2[e], xf[e] - mean[e], k3[e]))
                                   : fmaf(k1[e], dz, fmaf(k2[e], xf[e], k3[e]));
                 }
-                vstore_stream<T, V>(dx + row * g.K + p.col0, VT::pack(o));
+                col_store<T, V>(dx, g, p, row, VT::pack(o), sc1_ok);
             }
         }
     }

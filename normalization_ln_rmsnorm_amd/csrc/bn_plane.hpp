@@ -62,6 +62,23 @@ __device__ __forceinline__ int64_t plane_offset(const BnGeom &g, int64_t n, int 
     return (n * g.C + c) * g.HW;
 }
 
+// Output store of vector v of the plane that starts at element `off`.  A
+// plane under 4 GiB is addressed from its first element (the same in every
+// lane) and written with the device-scope buffer store; a larger one with a
+// non-temporal global store.
+template <typename T, int V>
+__device__ __forceinline__ void plane_store(T *out, int64_t off, int64_t v, const typename Vec<T, V>::raw_t &r,
+                                            bool sc1_ok) {
+    if (sc1_ok)
+        vstore_out<T, V>(out + off, (uint32_t)(v * V), r);
+    else
+        vstore_stream<T, V>(out + off + v * V, r);
+}
+template <typename T>
+__device__ __forceinline__ bool plane_sc1_ok(const BnGeom &g) {
+    return g.HW * (int64_t)sizeof(T) <= (int64_t)0xffffffff;
+}
+
 // -------------------------------------------------------- forward: stats
 template <typename T, int V>
 __global__ void __launch_bounds__(kBnBlock)
@@ -184,6 +201,7 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
     float a, s;
     bn_coeffs(mean, rstd, w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a, &s);
     const int64_t nvp = g.HW / V;
+    const bool sc1_ok = plane_sc1_ok<T>(g);
 
     for (int64_t n = n0; n < n1; ++n) {
         const int64_t off = plane_offset(g, n, c);
@@ -210,7 +228,7 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
                         if (RES) z += rf[e];
                         o[e] = act_fwd_io<T, ACT>(z, act_rt, act_p);
                     }
-                    vstore_stream<T, V>(y + off + v * V, VT::pack(o));
+                    plane_store<T, V>(y, off, v, VT::pack(o), sc1_ok);
                 }
             }
         }
@@ -238,6 +256,7 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
         s *= kGeluWScale;
     }
     const int64_t nvp = g.HW / V;
+    const bool sc1_ok = plane_sc1_ok<T>(g);
 
     // Accumulation.  Float32 I/O: float64 per element, so x - mean and
     // dz * (x - mean) are exact -- the 1e-5 tolerance on the channel sums
@@ -288,7 +307,7 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
                         s_dzx = fma(d, xc, s_dzx);
                         if (kExact) s_xc += xc;
                     }
-                    if (RES) vstore_stream<T, V>(dres + off + v * V, VT::pack(dz));
+                    if (RES) plane_store<T, V>(dres, off, v, VT::pack(dz), sc1_ok);
                 }
             }
         }
@@ -388,6 +407,7 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
         s *= kGeluWScale;
     }
     const int64_t nvp = g.HW / V;
+    const bool sc1_ok = plane_sc1_ok<T>(g);
     const T *dzsrc = DZ_SRC == 1 ? dres : dy;
 
     for (int64_t n = n0; n < n1; ++n) {
@@ -421,7 +441,7 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
                         }
                         o[e] = kExact ? fmaf(k1, dz, fmaf(k2, xf[e] - mean, k3)) : fmaf(k1, dz, fmaf(k2, xf[e], k3m));
                     }
-                    vstore_stream<T, V>(dx + off + v * V, VT::pack(o));
+                    plane_store<T, V>(dx, off, v, VT::pack(o), sc1_ok);
                 }
             }
         }

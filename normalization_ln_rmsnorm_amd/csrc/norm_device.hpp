@@ -138,14 +138,38 @@ template <typename T, int V>
 __device__ __forceinline__ void vstore(T *p, const typename Vec<T, V>::raw_t &r) {
     *reinterpret_cast<typename Vec<T, V>::raw_t *>(p) = r;
 }
-// Streaming variants: the data is touched once, so mark it non-temporal.
+// Streaming loads: the data is read once, so mark it non-temporal.
 template <typename T, int V>
 __device__ __forceinline__ typename Vec<T, V>::raw_t vload_stream(const T *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const typename Vec<T, V>::raw_t *>(p));
 }
+// Non-temporal streaming store.
 template <typename T, int V>
 __device__ __forceinline__ void vstore_stream(T *p, const typename Vec<T, V>::raw_t &r) {
     __builtin_nontemporal_store(r, reinterpret_cast<typename Vec<T, V>::raw_t *>(p));
+}
+// Streaming stores.  On gfx950, stores tagged with device scope (sc1) and no
+// non-temporal hint stream faster than non-temporal ones (RMSNorm 16384 x
+// 4096 bf16 backward: 64.0 vs 70.6 us for the same kernel, loads unchanged).
+// A global store cannot carry that tag from C++, so the store goes through a
+// raw buffer resource over `base`.  `base` must be the same in every lane of
+// the wave (it is then held in scalar registers; otherwise the compiler
+// serialises the store over the distinct values), and `idx` is the lane's
+// element offset from it, below 2^32 bytes.
+constexpr int kStoreCachePolicy = 0x10;  // sc1 = 1, sc0 = 0, nt = 0
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t store_rsrc(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)0xffffffffu, 0x00020000);
+}
+template <typename T, int V>
+__device__ __forceinline__ void vstore_out(T *base, uint32_t idx, const typename Vec<T, V>::raw_t &r) {
+    const int off = (int)(idx * (uint32_t)sizeof(T));
+    using raw_t = typename Vec<T, V>::raw_t;
+    if constexpr (sizeof(raw_t) == 16)
+        __builtin_amdgcn_raw_buffer_store_b128(r, store_rsrc(base), off, 0, kStoreCachePolicy);
+    else if constexpr (sizeof(raw_t) == 4)
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)r, store_rsrc(base), off, 0, kStoreCachePolicy);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)r, store_rsrc(base), off, 0, kStoreCachePolicy);
 }
 
 // Scalar parameter load (w, b, statistics) widened to float.

@@ -23,7 +23,8 @@
 // visits, the row slots of a block are combined in LDS, and each block
 // writes one partial row to the workspace ([NormPage] "Engineering tricks":
 // per-row-block partials followed by a sum).  A second kernel adds the
-// partial rows in a fixed order (float64), so dw/db are reproducible.#pragma once
+// partial rows in a fixed order (float64), so dw/db are reproducible.
+#pragma once
 
 #include "row_common.hpp"
 
@@ -184,7 +185,7 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
         for (int k = 0; k < IT; ++k) opaque(xr[k]);
 
         if (active) {
-            T *yrow = y + row * N;
+            T *ygrp = y + base * N;  // the block's row group: the same in every lane
 #pragma unroll
             for (int k = 0; k < IT; ++k) {
                 const int v = lane + k * tpr;
@@ -195,7 +196,7 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
                     VT::unpack(br[k], bf);
 #pragma unroll
                     for (int e = 0; e < V; ++e) o[e] = (f[e] - mean) * rstd * wf[e] + bf[e];
-                    vstore_stream<T, V>(yrow + (int64_t)v * V, VT::pack(o));
+                    vstore_out<T, V>(ygrp, (uint32_t)(slot_in_block * N + v * V), VT::pack(o));
                 }
             }
             if (lane == 0) {
@@ -231,6 +232,7 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
     const int lane = threadIdx.x & (tpr - 1);
     const int rpb = blockDim.x / tpr;
     const int slot_in_block = threadIdx.x / tpr;
+    const bool full_rows = nv == tpr * IT;  // every thread's IT vectors lie inside the row
 
     raw_t wr[IT];
 #pragma unroll
@@ -281,14 +283,23 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
         const int64_t nrow = row + step;
         raw_t nx[IT], nd[IT];
         float nmean = 0.0f, nrstd = 0.0f;
+        if (full_rows && base + step + rpb <= M) {  // block-uniform: every slot's next row is in range
 #pragma unroll
-        for (int k = 0; k < IT; ++k) {
-            const int v = lane + k * tpr;
-            nx[k] = zeros_raw<VT>();
-            nd[k] = zeros_raw<VT>();
-            if (nrow < M && v < nv) {
+            for (int k = 0; k < IT; ++k) {
+                const int v = lane + k * tpr;
                 nx[k] = vload_stream<T, V>(x + nrow * N + (int64_t)v * V);
                 nd[k] = vload_stream<T, V>(dy + nrow * N + (int64_t)v * V);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < IT; ++k) {
+                const int v = lane + k * tpr;
+                nx[k] = zeros_raw<VT>();
+                nd[k] = zeros_raw<VT>();
+                if (nrow < M && v < nv) {
+                    nx[k] = vload_stream<T, V>(x + nrow * N + (int64_t)v * V);
+                    nd[k] = vload_stream<T, V>(dy + nrow * N + (int64_t)v * V);
+                }
             }
         }
         if (nrow < M) {
@@ -299,8 +310,10 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
         for (int k = 0; k < IT; ++k) opaque(wr[k]);  // keep w packed (no hoisted float copy)
 
         // Pass 1: the row sums and the column partials.  Out-of-range
-        // elements hold x = dy = 0 and add nothing (their g is 0).
+        // elements hold x = dy = 0 and add nothing (their g is 0).  g is
+        // kept in float32 for pass 2, which then needs neither dy nor w.
         float s_gx = 0.0f, s_g = 0.0f;
+        float gr[IT][V];
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             float xf[V], df[V], wf[V];
@@ -309,43 +322,44 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
             VT::unpack(wr[k], wf);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                const float xh = (xf[e] - mean) * rstd;
+                const float xh = (RMS ? xf[e] : xf[e] - mean) * rstd;
                 acc_w[k][e] = fmaf(df[e], xh, acc_w[k][e]);
                 if (!RMS) acc_b[k][e] += df[e];
                 const float g = df[e] * wf[e];
+                gr[k][e] = g;
                 s_gx = fmaf(g, xh, s_gx);
-                s_g += g;
+                if (!RMS) s_g += g;
             }
         }
-        if (RMS) s_g = 0.0f;
         row_sum2(s_gx, s_g, tpr, lds, slot);
         slot ^= 1;
+        // dx = rstd * (g - c_g - xhat * c_gx) with xhat = (x - mean) * rstd,
+        // evaluated as rstd * g + ((x - mean) * k1 + k0): two FMAs per
+        // element after the centring subtraction (none for RMSNorm).
         const float c_gx = s_gx * inv_n, c_g = s_g * inv_n;
+        const float k1 = -(rstd * rstd) * c_gx;
+        const float k0 = -rstd * c_g;
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             opaque(rx[k]);
-            opaque(rd[k]);
             opaque(wr[k]);
         }
 
-        // Pass 2: dx from the packed row.
+        // Pass 2: dx from the packed x and the float32 g.
         if (active) {
-            T *dxrow = dx + row * N;
+            T *dxgrp = dx + base * N;  // the block's row group: the same in every lane
 #pragma unroll
             for (int k = 0; k < IT; ++k) {
                 const int v = lane + k * tpr;
                 if (v < nv) {
-                    float xf[V], df[V], wf[V], o[V];
+                    float xf[V], o[V];
                     VT::unpack(rx[k], xf);
-                    VT::unpack(rd[k], df);
-                    VT::unpack(wr[k], wf);
 #pragma unroll
                     for (int e = 0; e < V; ++e) {
-                        const float xh = (xf[e] - mean) * rstd;
-                        const float g = df[e] * wf[e];
-                        o[e] = rstd * (g - c_g - xh * c_gx);
+                        const float lin = RMS ? xf[e] * k1 : fmaf(xf[e] - mean, k1, k0);
+                        o[e] = fmaf(gr[k][e], rstd, lin);
                     }
-                    vstore_stream<T, V>(dxrow + (int64_t)v * V, VT::pack(o));
+                    vstore_out<T, V>(dxgrp, (uint32_t)(slot_in_block * N + v * V), VT::pack(o));
                 }
             }
         }
