@@ -33,6 +33,10 @@ constexpr int kBnUnrollStream = 8;       // the same for the plane apply and dx 
                                          // the bf16 GELU dx pass 204.6 -> 199.8 us and apply
                                          // 143.9 -> 141.0 us; the VALU-bound reduction, 143 ->
                                          // 147 us, keeps 4)
+constexpr int64_t kBnStatsChunk = (int64_t)kBnBlock * kBnUnroll * 64;  // vectors of a plane
+                                         // after which a thread's float32 statistics state
+                                         // moves into float64 (64 x 4 vectors per thread:
+                                         // 1024 float32 or 2048 16-bit values)
 
 // Which activations take the fast (published-approximation) forms of GELU:
 // the forward only for bf16 (fp16's 11-bit significand resolves the
@@ -96,6 +100,15 @@ __device__ __forceinline__ WelfF wave_merge(WelfF s) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
         WelfF o{shfl_xor_f(s.n, m), shfl_xor_f(s.mean, m), shfl_xor_f(s.m2, m)};
+        s = welf_merge(s, o);
+    }
+    return s;
+}
+
+__device__ __forceinline__ WelfD wave_merge(WelfD s) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        WelfD o{shfl_xor_d(s.n, m), shfl_xor_d(s.mean, m), shfl_xor_d(s.m2, m)};
         s = welf_merge(s, o);
     }
     return s;

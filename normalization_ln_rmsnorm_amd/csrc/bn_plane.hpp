@@ -89,42 +89,62 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, double *__restrict__ part) {
     tile_of_block(g, &c, &n0, &n1);
     const int64_t nvp = g.HW / V;  // vectors per plane
 
+    // Each thread folds its chunks into a float32 running state.  A plane
+    // longer than kBnStatsChunk vectors (then the whole tile) is walked in
+    // pieces of that many vectors, after each of which the state moves into
+    // a float64 one: a float32 state never spans more than 1024 float32 or
+    // 2048 16-bit values per thread (a single 4 GiB plane is one tile).
+    // Shorter planes keep the float32 state and wave merge throughout.
+    const bool long_plane = nvp > kBnStatsChunk;  // the same in every lane
     WelfF st{0.0f, 0.0f, 0.0f};
+    WelfD acc{0.0, 0.0, 0.0};
     for (int64_t n = n0; n < n1; ++n) {
         const T *p = x + plane_offset(g, n, c);
-        for (int64_t v0 = threadIdx.x; v0 < nvp; v0 += (int64_t)kBnBlock * kBnUnroll) {
-            raw_t r[kBnUnroll];
+        for (int64_t vc = 0; vc < nvp; vc += kBnStatsChunk) {
+            const int64_t ve = nvp - vc > kBnStatsChunk ? vc + kBnStatsChunk : nvp;
+            for (int64_t v0 = vc + threadIdx.x; v0 < ve; v0 += (int64_t)kBnBlock * kBnUnroll) {
+                raw_t r[kBnUnroll];
 #pragma unroll
-            for (int u = 0; u < kBnUnroll; ++u) {
-                const int64_t v = v0 + (int64_t)u * kBnBlock;
-                if (v < nvp) r[u] = vload_stream<T, V>(p + v * V);
-            }
-#pragma unroll
-            for (int u = 0; u < kBnUnroll; ++u) {
-                const int64_t v = v0 + (int64_t)u * kBnBlock;
-                if (v < nvp) {
-                    float f[V];
-                    VT::unpack(r[u], f);
-                    float s = 0.0f;
-#pragma unroll
-                    for (int e = 0; e < V; ++e) s += f[e];
-                    const float cm = s * (1.0f / V);
-                    float cm2 = 0.0f;
-#pragma unroll
-                    for (int e = 0; e < V; ++e) {
-                        const float d = f[e] - cm;
-                        cm2 = fmaf(d, d, cm2);
-                    }
-                    welf_fold(st, (float)V, cm, cm2);
+                for (int u = 0; u < kBnUnroll; ++u) {
+                    const int64_t v = v0 + (int64_t)u * kBnBlock;
+                    if (v < ve) r[u] = vload_stream<T, V>(p + v * V);
                 }
+#pragma unroll
+                for (int u = 0; u < kBnUnroll; ++u) {
+                    const int64_t v = v0 + (int64_t)u * kBnBlock;
+                    if (v < ve) {
+                        float f[V];
+                        VT::unpack(r[u], f);
+                        float s = 0.0f;
+#pragma unroll
+                        for (int e = 0; e < V; ++e) s += f[e];
+                        const float cm = s * (1.0f / V);
+                        float cm2 = 0.0f;
+#pragma unroll
+                        for (int e = 0; e < V; ++e) {
+                            const float d = f[e] - cm;
+                            cm2 = fmaf(d, d, cm2);
+                        }
+                        welf_fold(st, (float)V, cm, cm2);
+                    }
+                }
+            }
+            if (long_plane) {
+                acc = welf_merge(acc, WelfD{st.n, st.mean, st.m2});
+                st = WelfF{0.0f, 0.0f, 0.0f};
             }
         }
     }
-    st = wave_merge(st);
+    if (long_plane) {
+        acc = wave_merge(acc);
+    } else {
+        st = wave_merge(st);
+        acc = WelfD{st.n, st.mean, st.m2};
+    }
 
     __shared__ WelfD wave_part[kBnWaves];
     const int wave = threadIdx.x / kWave;
-    if ((threadIdx.x & (kWave - 1)) == 0) wave_part[wave] = WelfD{st.n, st.mean, st.m2};
+    if ((threadIdx.x & (kWave - 1)) == 0) wave_part[wave] = acc;
     __syncthreads();
     if (threadIdx.x == 0) {
         WelfD acc = wave_part[0];
@@ -269,15 +289,22 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
     constexpr bool kExact = sizeof(T) == 4;
     using Acc = typename std::conditional<kExact, double, float>::type;
     Acc s_dz = 0, s_dzx = 0, s_xc = 0;
+    // 16-bit I/O: a plane longer than kBnStatsChunk vectors is walked in
+    // pieces of that many, after each of which the float32 sums move into
+    // float64 ones, so none spans more than 2048 values per thread.
+    const bool long_plane = nvp > kBnStatsChunk;  // the same in every lane
+    double f_dz = 0.0, f_dzx = 0.0;
     const Acc mean_a = kExact ? (Acc)mean : (Acc)0;
     for (int64_t n = n0; n < n1; ++n) {
         const int64_t off = plane_offset(g, n, c);
-        for (int64_t v0 = threadIdx.x; v0 < nvp; v0 += (int64_t)kBnBlock * kBnUnroll) {
+        for (int64_t vc = 0; vc < nvp; vc += kBnStatsChunk) {
+          const int64_t ve = nvp - vc > kBnStatsChunk ? vc + kBnStatsChunk : nvp;
+          for (int64_t v0 = vc + threadIdx.x; v0 < ve; v0 += (int64_t)kBnBlock * kBnUnroll) {
             raw_t rd[kBnUnroll], rx[kBnUnroll], rr[kBnUnroll];
 #pragma unroll
             for (int u = 0; u < kBnUnroll; ++u) {
                 const int64_t v = v0 + (int64_t)u * kBnBlock;
-                if (v < nvp) {
+                if (v < ve) {
                     rd[u] = vload_stream<T, V>(dy + off + v * V);
                     rx[u] = vload_stream<T, V>(x + off + v * V);
                     if (RES && ACT != kActNone) rr[u] = vload_stream<T, V>(res + off + v * V);
@@ -286,7 +313,7 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
 #pragma unroll
             for (int u = 0; u < kBnUnroll; ++u) {
                 const int64_t v = v0 + (int64_t)u * kBnBlock;
-                if (v < nvp) {
+                if (v < ve) {
                     float df[V], xf[V], rf[V], dz[V];
                     VT::unpack(rd[u], df);
                     VT::unpack(rx[u], xf);
@@ -310,10 +337,16 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
                     if (RES) plane_store<T, V>(dres, off, v, VT::pack(dz), sc1_ok);
                 }
             }
+          }
+          if (!kExact && long_plane) {
+              f_dz += (double)s_dz;
+              f_dzx += (double)s_dzx;
+              s_dz = s_dzx = 0;
+          }
         }
     }
-    const double t_dz = wave_sum_d((double)s_dz);
-    const double t_dzx = wave_sum_d((double)s_dzx);
+    const double t_dz = wave_sum_d((double)s_dz + f_dz);
+    const double t_dzx = wave_sum_d((double)s_dzx + f_dzx);
     const double t_xc = wave_sum_d((double)s_xc);
     __shared__ double wave_part[kBnWaves][3];
     const int wave = threadIdx.x / kWave;

@@ -214,3 +214,123 @@ def test_backward_bitwise_deterministic(orc):
     torch.cuda.synchronize()
     for a, b_ in zip(outs[0], outs[1]):
         assert torch.equal(a, b_)
+
+
+# ---------------------------------------------------------------- output stores past 2 GiB
+# The output stores address a plane (plane path) or a row tile (column path)
+# from its first element with 32-bit offsets, and fall back to non-temporal
+# global stores when that region is 4 GiB or more.  Replicating an input
+# block along the batch or spatial axis leaves every per-channel mean the
+# statistics and the backward sums are made of unchanged, so the outputs of
+# the large tensor are the oracle's outputs on the block, repeated (dw / db
+# scale with the replication; the running variance's n / (n - 1) uses the
+# large count).  Each repeated output is checked through its maximum and
+# minimum over the copies: both within tolerance bound every copy.  The
+# block's channels keep the workload recipe's ratio of mean to spread (at
+# most ~4): float32 statistics cannot meet the 1e-5 tolerance on y for a
+# channel whose mean is hundreds of spreads from zero.
+def run_replicated(orc, dtype, small, reps, axis, act, residual, x=None):
+    Nb0, C, HW0 = small
+    wl = _wl(dtype, act, residual)
+    inp = gen_bn(wl, Nb=Nb0, C=C, HW=HW0)
+    if x is not None:
+        inp["x"] = x
+    eps, mom, bf16 = wl.eps, wl.momentum, dtype == "bf16"
+    rep = tuple(reps if d == axis else 1 for d in range(3))
+
+    def big(a):
+        return to_dev(a, dtype).repeat(*rep)
+
+    x, dy = big(inp["x"]), big(inp["dy"])
+    res = big(inp["res"]) if residual else None
+    w, b = to_dev(inp["w"], dtype), to_dev(inp["b"], dtype)
+    rm = torch.from_numpy(inp["running_mean"].copy()).cuda()
+    rv = torch.from_numpy(inp["running_var"].copy()).cuda()
+    y, sm, sr = nl.bn_fwd_train(x, w, b, rm, rv, eps, mom, act, res)
+    dx, dres, dw, db = nl.bn_bwd(dy, x, w, b, sm, sr, act, res)
+    ye = nl.bn_fwd_eval(x, w, b, rm, rv, eps, act, res)
+    torch.cuda.synchronize()
+    del x, dy, res
+
+    res_np = inp["res"] if residual else None
+    ry, rsm, rsr, rrm, rrv = orc.bn_fwd_train(inp["x"], res_np, inp["w"], inp["b"], inp["running_mean"],
+                                              inp["running_var"], eps=eps, momentum=mom, act=act, bf16=bf16)
+    rdx, rdres, rdw, rdb = orc.bn_bwd(inp["dy"], inp["x"], res_np, inp["w"], inp["b"], eps=eps, act=act,
+                                      bf16=bf16)
+    rye = orc.bn_fwd_eval(inp["x"], to_f64(rm), to_f64(rv), res_np, inp["w"], inp["b"], eps=eps, act=act,
+                          bf16=bf16)
+    # Running variance with the replicated count n instead of the block's n0.
+    n0, n = Nb0 * HW0, Nb0 * HW0 * reps
+    rv0 = orc.widen(inp["running_var"], bf16=False)
+    var = (rrv - (1.0 - mom) * rv0) / mom * (n0 - 1) / n0
+    rrv_big = (1.0 - mom) * rv0 + mom * var * n / (n - 1)
+
+    def folds(t):
+        if axis == 0:
+            v = t.view(reps, Nb0, C, HW0)
+            return v.amax(0), v.amin(0)
+        v = t.view(Nb0, C, reps, HW0)
+        return v.amax(2), v.amin(2)
+
+    tag = f"bn/{dtype}/{small}x{reps}@{axis}/{act}/res={residual}"
+    ch = (0, 2)
+    for name, t, ref in (("y", y, ry), ("y_eval", ye, rye), ("dx", dx, rdx)) + (
+            (("dres", dres, rdres),) if residual else ()):
+        hi, lo = folds(t)
+        scale = None
+        if name == "dx":
+            scale = np.abs(rdx).max(axis=ch, keepdims=True) + np.abs(orc.widen(inp["w"], bf16=bf16)
+                                                                     * rsr)[None, :, None]
+        check(f"{tag} {name} max", to_f64(hi), ref, dtype, group_axis=ch, scale=scale)
+        check(f"{tag} {name} min", to_f64(lo), ref, dtype, group_axis=ch, scale=scale)
+    check(f"{tag} save_mean", to_f64(sm), rsm, "f32")
+    check(f"{tag} save_rstd", to_f64(sr), rsr, "f32")
+    check(f"{tag} running_mean", to_f64(rm), rrm, "f32")
+    check(f"{tag} running_var", to_f64(rv), rrv_big, "f32")
+    # dw and db add `reps` copies of the block's terms, each copy carrying
+    # the same per-element rounding, so they are compared per copy.
+    check(f"{tag} dw / copies", to_f64(dw) / reps, rdw, dtype)
+    check(f"{tag} db / copies", to_f64(db) / reps, rdb, dtype)
+
+
+@pytest.mark.parametrize("HW", [(1 << 30) - 1024, 1 << 30])
+def test_plane_over_2_and_4_gib(orc, HW):
+    """One float32 plane of 4 GiB - 4 KiB (buffer stores at offsets past
+    2^31) and of 4 GiB (the non-temporal fallback)."""
+    print(f"case bn plane f32 1x1x{HW}", flush=True)
+    run_replicated(orc, "f32", (1, 1, 1024), HW // 1024, 2, "relu", True)
+
+
+def two_row_block(C, seed):
+    """Rows m_c + s_c and m_c - s_c with the workload recipe's channel mean
+    m_c ~ U(-2, 2) and spread s_c ~ U(0.5, 3), float32 [2, C, 1].  Two free
+    draws per channel would give some of millions of channels a spread so
+    small that no float32 statistics reach the 1e-5 tolerance on y."""
+    rng = np.random.default_rng(seed)
+    m = rng.uniform(-2.0, 2.0, C)
+    sp = rng.uniform(0.5, 3.0, C)
+    return np.stack([m + sp, m - sp]).astype(np.float32)[:, :, None]
+
+
+def test_column_tile_over_2_gib(orc):
+    """Column path, float32, 256-row tiles of 2^22 - 16 columns (4 GiB -
+    16 KiB: buffer stores at offsets past 2^31)."""
+    C = (1 << 22) - 16
+    print(f"case bn cols f32 256x{C}", flush=True)
+    run_replicated(orc, "f32", (2, C, 1), 128, 0, "gelu", True, x=two_row_block(C, 20251))
+
+
+@pytest.mark.parametrize("dtype,act,residual", [("f32", "relu", True), ("bf16", "none", False)])
+def test_column_tile_fallback(orc, dtype, act, residual):
+    """Column path with a nominal row tile of 4 GiB (2^22 columns): the
+    non-temporal fallback, checked element by element.  Every channel has
+    two elements, so its tolerance floor (2^-12 of the channel's largest
+    output) is sound only while one of them is far from zero: float32 runs
+    ReLU + residual (every store: y, dres, dx, y_eval); bf16, whose
+    tolerance leans on that floor, runs the plain affine output (one element
+    near +|w|, the other near -|w|)."""
+    C = 1 << 22
+    inp = gen_bn(_wl(dtype, act, residual), Nb=2, C=C, HW=1)
+    inp["x"] = to_io(two_row_block(C, 20252), dtype)
+    print(f"case bn cols fallback {dtype} 2x{C} {act} res={residual}", flush=True)
+    run_case(orc, dtype, 2, C, 1, act, residual, inp=inp)
