@@ -214,3 +214,52 @@ def test_empty_batch_is_noop(orc):
     dx, dw, db = nl.ln_bwd(x, x, torch.ones(64, device="cuda"), mean, rstd)
     torch.cuda.synchronize()
     assert torch.all(dw == 0) and torch.all(db == 0)
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+def test_rows_past_2_32_elements(orc, kind):
+    """bf16, 2^20 + 64 rows x 4096 (2^32 + 2^18 elements, 8 GiB per tensor):
+    every element index of the row path beyond 32 bits.  Rows are
+    independent, so a 64-row block repeated down the rows has the oracle's
+    block outputs in every copy; each output is checked through its maximum
+    and minimum over the copies (both within tolerance bound every copy),
+    and dw / db, which add the copies, per copy."""
+    dtype, N, B, reps = "bf16", 4096, 64, (1 << 14) + 1
+    wl = _wl(kind, dtype)
+    inp = gen_rowwise(wl, M=B, N=N)
+    x = to_dev(inp["x"], dtype).repeat(reps, 1)
+    dy = to_dev(inp["dy"], dtype).repeat(reps, 1)
+    w = to_dev(inp["w"], dtype)
+    print(f"case {kind} bf16 {B * reps}x{N}", flush=True)
+    if kind == "ln":
+        b = to_dev(inp["b"], dtype)
+        y, mean, rstd = nl.ln_fwd(x, w, b, wl.eps)
+        dx, dw, db = nl.ln_bwd(dy, x, w, mean, rstd)
+        ry, rmean, rrstd = orc.ln_fwd(inp["x"], inp["w"], inp["b"], eps=wl.eps, bf16=True)
+        rdx, rdw, rdb = orc.ln_bwd(inp["dy"], inp["x"], inp["w"], eps=wl.eps, bf16=True)
+    else:
+        y, rstd = nl.rms_fwd(x, w, wl.eps)
+        dx, dw = nl.rms_bwd(dy, x, w, rstd)
+        mean = db = None
+        ry, rrstd = orc.rms_fwd(inp["x"], inp["w"], eps=wl.eps, bf16=True)
+        rdx, rdw = orc.rms_bwd(inp["dy"], inp["x"], inp["w"], eps=wl.eps, bf16=True)
+    torch.cuda.synchronize()
+    del x, dy
+
+    def folds(t):
+        v = t.view(reps, B, -1)
+        return v.amax(0), v.amin(0)
+
+    g = np.abs(orc.widen(inp["dy"], bf16=True) * orc.widen(inp["w"], bf16=True))
+    dx_scale = rrstd[:, None] * g.max(axis=1, keepdims=True)
+    tag = f"{kind}/bf16/{B}x{reps}x{N}"
+    for name, t, ref, dt, scale in (("y", y, ry, dtype, None), ("dx", dx, rdx, dtype, dx_scale),
+                                    ("rstd", rstd, rrstd[:, None], "f32", None)) + (
+            (("mean", mean, rmean[:, None], "f32", None),) if kind == "ln" else ()):
+        hi, lo = folds(t)
+        for side, v in (("max", hi), ("min", lo)):
+            check(f"{tag} {name} {side}", to_f64(v), ref, dt, group_axis=1 if dt != "f32" else None,
+                  scale=scale)
+    check(f"{tag} dw / copies", to_f64(dw) / reps, rdw, dtype)
+    if kind == "ln":
+        check(f"{tag} db / copies", to_f64(db) / reps, rdb, dtype)
