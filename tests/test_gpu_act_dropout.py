@@ -164,3 +164,35 @@ def test_fp16_gelu_forward_tail_is_relatively_accurate(orc):
     torch.cuda.synchronize()
     ref = orc.act_dropout_fwd(xs, "gelu", 0.0, 5, 0)
     check("fp16 gelu tail y", to_f64(y).reshape(-1, 64), ref.reshape(-1, 64), "f16", group_axis=1)
+
+
+def test_past_2_32_elements(orc):
+    """bf16, 2^32 + 2^20 + 3 elements (8 GiB per tensor, a ragged scalar
+    tail): the element index, the generator counter and the output offsets
+    beyond 32 bits.  The input repeats a 2^20-element block; slices around
+    2^31, 2^32 and the end are checked against the oracle with the offset of
+    their first element (the mask depends on seed and offset + index only)."""
+    B, L = 1 << 20, 8192
+    n = (1 << 32) + B + 3
+    reps = (n - 3) // B
+    seed, off0, p = 0x5EED, 12344, 0.1  # offsets are multiples of 4
+    inp = _inputs("bf16", B, seed=7)
+    xb, dyb = to_dev(inp["x"], "bf16"), to_dev(inp["dy"], "bf16")
+    x = torch.cat([xb.repeat(reps), xb[:3]])
+    dy = torch.cat([dyb.repeat(reps), dyb[:3]])
+    assert x.numel() == n
+    print(f"case act_dropout bf16 n={n}", flush=True)
+    y = nl.act_dropout_fwd(x, "gelu", p, seed, off0)
+    dx = nl.act_dropout_bwd(dy, x, "gelu", p, seed, off0)
+    torch.cuda.synchronize()
+    del x, dy
+    p32 = float(np.float32(p))
+    xs_all = np.concatenate([inp["x"], inp["x"]])
+    dys_all = np.concatenate([inp["dy"], inp["dy"]])
+    for s, ln in ((0, L), ((1 << 31) - L // 2, L), ((1 << 32) - L // 2, L), (n - L - 3, L + 3)):
+        k = s % B
+        xs, dys = xs_all[k:k + ln], dys_all[k:k + ln]
+        ry = orc.act_dropout_fwd(xs, "gelu", p32, seed, off0 + s, bf16=True)
+        rdx = orc.act_dropout_bwd(dys, xs, "gelu", p32, seed, off0 + s, bf16=True)
+        check(f"ad/bf16/n={n}/slice@{s} y", to_f64(y[s:s + ln]), ry, "bf16")
+        check(f"ad/bf16/n={n}/slice@{s} dx", to_f64(dx[s:s + ln]), rdx, "bf16")
