@@ -114,11 +114,6 @@ __device__ __forceinline__ WelfD wave_merge(WelfD s) {
     return s;
 }
 
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_d(v, m);
-    return v;
-}
 
 // ------------------------------------------------- backward coefficients
 // With m the saved (float32) mean, the channel sums are S_dz = sum dz,

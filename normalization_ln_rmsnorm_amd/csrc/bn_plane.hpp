@@ -168,21 +168,49 @@ __device__ __forceinline__ WelfD merge_channel_tiles(const double *__restrict__ 
     __shared__ WelfD sh;
     if (threadIdx.x < kWave) {
         const double *q = part + (int64_t)c * tiles * 3;
-        double sn = 0.0, snm = 0.0;
-        for (int t = threadIdx.x; t < tiles; t += kWave) {
-            sn += q[t * 3 + 0];
-            snm = fma(q[t * 3 + 0], q[t * 3 + 1], snm);
+        const int lane = threadIdx.x;
+        double sn = 0.0, snm = 0.0, m2 = 0.0, mean;
+        constexpr int R = 4;  // tiles held per lane on the one-round path
+        if (tiles <= R * kWave) {  // the same in every lane: one round of loads
+            double tn[R], tm[R], tq[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int t = lane + r * kWave;
+                tn[r] = tm[r] = tq[r] = 0.0;
+                if (t < tiles) {
+                    tn[r] = q[t * 3 + 0];
+                    tm[r] = q[t * 3 + 1];
+                    tq[r] = q[t * 3 + 2];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                sn += tn[r];
+                snm = fma(tn[r], tm[r], snm);
+            }
+            sn = wave_sum_dpp_d(sn);
+            snm = wave_sum_dpp_d(snm);
+            mean = snm / sn;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {  // absent tiles have n = M2 = 0
+                const double d = tm[r] - mean;
+                m2 += fma(tn[r] * d, d, tq[r]);
+            }
+        } else {
+            for (int t = lane; t < tiles; t += kWave) {
+                sn += q[t * 3 + 0];
+                snm = fma(q[t * 3 + 0], q[t * 3 + 1], snm);
+            }
+            sn = wave_sum_dpp_d(sn);
+            snm = wave_sum_dpp_d(snm);
+            mean = snm / sn;
+            for (int t = lane; t < tiles; t += kWave) {
+                const double d = q[t * 3 + 1] - mean;
+                m2 += fma(q[t * 3 + 0] * d, d, q[t * 3 + 2]);
+            }
         }
-        sn = wave_sum_d(sn);
-        snm = wave_sum_d(snm);
-        const double mean = snm / sn;
-        double m2 = 0.0;
-        for (int t = threadIdx.x; t < tiles; t += kWave) {
-            const double d = q[t * 3 + 1] - mean;
-            m2 += fma(q[t * 3 + 0] * d, d, q[t * 3 + 2]);
-        }
-        m2 = wave_sum_d(m2);
-        if (threadIdx.x == 0) sh = WelfD{sn, mean, m2};
+        m2 = wave_sum_dpp_d(m2);
+        if (lane == 0) sh = WelfD{sn, mean, m2};
     }
     __syncthreads();
     return sh;

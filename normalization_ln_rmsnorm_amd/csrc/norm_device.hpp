@@ -214,6 +214,37 @@ __device__ __forceinline__ float seg_sum(float v, int seg) {
     return v;
 }
 
+// Full-wave float64 sum with the same lane pattern (each 64-bit value moves
+// as its two 32-bit halves); every lane receives the sum.  All 64 lanes must
+// be active.
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double swz_xor16_d(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)u, 0x401F);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(u >> 32), 0x401F);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double lane_read_d(double v, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double wave_sum_dpp_d(double v) {
+    v += dpp_d<kDppXor1>(v);
+    v += dpp_d<kDppXor2>(v);
+    v += dpp_d<kDppHalfMirror>(v);
+    v += dpp_d<kDppMirror>(v);
+    v += swz_xor16_d(v);
+    return lane_read_d(v, 0) + lane_read_d(v, 32);
+}
+
 // Two sums at once (keeps the dependency chains interleaved).
 __device__ __forceinline__ void seg_sum2(float &a, float &b, int seg) {
     if (seg > 1) { a += dpp<kDppXor1>(a); b += dpp<kDppXor1>(b); }
@@ -227,11 +258,15 @@ __device__ __forceinline__ void seg_sum2(float &a, float &b, int seg) {
     }
 }
 
-// Full-wave butterfly on doubles through ds_bpermute (used once per
-// workgroup in the BatchNorm reductions, where float64 accumulation keeps
-// the channel sums exact enough).
+// Lane exchange of doubles through ds_bpermute, for the float64 Welford
+// wave merges (each step merges with the lane `mask` away).
 __device__ __forceinline__ double shfl_xor_d(double v, int mask) {
     return __shfl_xor(v, mask, kWave);
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_d(v, m);
+    return v;
 }
 
 // Workgroups are dispatched to the chip's 8 XCDs round-robin by linear
