@@ -334,3 +334,14 @@ def test_column_tile_fallback(orc, dtype, act, residual):
     inp["x"] = to_io(two_row_block(C, 20252), dtype)
     print(f"case bn cols fallback {dtype} 2x{C} {act} res={residual}", flush=True)
     run_case(orc, dtype, 2, C, 1, act, residual, inp=inp)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_long_planes(orc, dtype):
+    """Planes of 2^21 + 512 elements: past 2^18 vectors for every I/O type,
+    so the statistics (and, for 16-bit I/O, the backward reduction) move
+    their float32 state into float64 between pieces of the plane; checked
+    element by element."""
+    HW = (1 << 21) + 512
+    print(f"case bn long planes {dtype} 2x3x{HW}", flush=True)
+    run_case(orc, dtype, 2, 3, HW, "gelu", True)
