@@ -143,7 +143,8 @@ template <typename T, int V>
 __device__ __forceinline__ typename Vec<T, V>::raw_t vload_stream(const T *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const typename Vec<T, V>::raw_t *>(p));
 }
-// Non-temporal streaming store.
+// Non-temporal streaming store: the fallback where an output region is
+// 4 GiB or more (vstore_out below needs 32-bit offsets from its base).
 template <typename T, int V>
 __device__ __forceinline__ void vstore_stream(T *p, const typename Vec<T, V>::raw_t &r) {
     __builtin_nontemporal_store(r, reinterpret_cast<typename Vec<T, V>::raw_t *>(p));
