@@ -101,11 +101,28 @@ bn_col_stats_kernel(const T *__restrict__ x, BnColGeom g, double *__restrict__ p
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
     const ColPos p = col_pos(g, V);
-    float n = 0.0f, mean[V], m2[V];
+    // Float32 I/O: a column whose first two rows in the tile lie more than
+    // four times their difference from zero is folded relative to the first
+    // row's value, so the float32 state's rounding scales with the spread
+    // rather than the mean; otherwise (and for 16-bit I/O) no shift, since a
+    // shift a few spreads from a near-zero mean would enlarge the rounding.
+    // The shift depends only on the tile and column, so the row slices of a
+    // column agree.
+    float n = 0.0f, mean[V], m2[V], shift[V];
 #pragma unroll
-    for (int e = 0; e < V; ++e) mean[e] = m2[e] = 0.0f;
+    for (int e = 0; e < V; ++e) mean[e] = m2[e] = shift[e] = 0.0f;
     if (p.active) {
         const T *base = x + p.col0;
+        if constexpr (sizeof(T) == 4) {
+            if (p.r0 + 1 < p.r1) {
+                float f0[V], f1[V];
+                VT::unpack(vload<T, V>(base + p.r0 * g.K), f0);
+                VT::unpack(vload<T, V>(base + (p.r0 + 1) * g.K), f1);
+#pragma unroll
+                for (int e = 0; e < V; ++e)
+                    shift[e] = fabsf(f0[e]) > 4.0f * fabsf(f0[e] - f1[e]) ? f0[e] : 0.0f;
+            }
+        }
         const int64_t step = (int64_t)g.RPP;
         for (int64_t r = p.r0 + p.rs; r < p.r1; r += step * kBnUnroll) {
             raw_t buf[kBnUnroll];
@@ -124,9 +141,10 @@ bn_col_stats_kernel(const T *__restrict__ x, BnColGeom g, double *__restrict__ p
                     const float inv = 1.0f / n;
 #pragma unroll
                     for (int e = 0; e < V; ++e) {
-                        const float d = f[e] - mean[e];
+                        const float fs = f[e] - shift[e];
+                        const float d = fs - mean[e];
                         mean[e] = fmaf(d, inv, mean[e]);
-                        m2[e] = fmaf(d, f[e] - mean[e], m2[e]);
+                        m2[e] = fmaf(d, fs - mean[e], m2[e]);
                     }
                 }
             }
@@ -140,7 +158,7 @@ bn_col_stats_kernel(const T *__restrict__ x, BnColGeom g, double *__restrict__ p
     sh_n[t] = n;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-        sh_mean[t * V + e] = mean[e];
+        sh_mean[t * V + e] = (double)mean[e] + shift[e];
         sh_m2[t * V + e] = m2[e];
     }
     for (int h = tree_start(g.RPP); h >= 1; h >>= 1) {
@@ -224,13 +242,14 @@ bn_col_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T 
     const ColPos p = col_pos(g, V);
     const bool sc1_ok = col_sc1_ok<T>(g);
     if (!p.active) return;  // no barriers in this kernel
-    float a[V], s[V];
+    float a[V], s[V], mn[V], bs[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
         const int64_t c = (p.col0 + e) / g.HW;
-        const float mean = mean_src[c];
+        mn[e] = mean_src[c];
+        bs[e] = b ? ld1(b + c) : 0.0f;
         const float rstd = MODE == 0 ? scale_src[c] : 1.0f / sqrtf(scale_src[c] + eps);
-        bn_coeffs(mean, rstd, w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a[e], &s[e]);
+        bn_coeffs(mn[e], rstd, w ? ld1(w + c) : 1.0f, bs[e], &a[e], &s[e]);
     }
     const int64_t step = (int64_t)g.RPP;
     for (int64_t r = p.r0 + p.rs; r < p.r1; r += step * kBnUnroll) {
@@ -252,7 +271,7 @@ bn_col_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T 
                 if (RES) VT::unpack(rr_[u], rf);
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    float z = fmaf(f[e], a[e], s[e]);
+                    float z = bn_pre<T>(f[e], a[e], s[e], mn[e], bs[e]);
                     if (RES) z += rf[e];
                     o[e] = act_fwd_io<T, ACT>(z, act_rt, act_p);
                 }
@@ -284,18 +303,19 @@ bn_col_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, cons
     const ColPos p = col_pos(g, V);
     const bool sc1_ok = col_sc1_ok<T>(g);
     Acc s_dz[V], s_dzx[V], s_xc[V];
-    float a[V], s[V], mean[V];
+    float a[V], s[V], mean[V], bs[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
         s_dz[e] = s_dzx[e] = s_xc[e] = 0;
-        a[e] = s[e] = mean[e] = 0.0f;
+        a[e] = s[e] = mean[e] = bs[e] = 0.0f;
     }
     if (p.active) {
 #pragma unroll
         for (int e = 0; e < V; ++e) {
             const int64_t c = (p.col0 + e) / g.HW;
             mean[e] = save_mean[c];
-            bn_coeffs(mean[e], save_rstd[c], w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a[e], &s[e]);
+            bs[e] = b ? ld1(b + c) : 0.0f;
+            bn_coeffs(mean[e], save_rstd[c], w ? ld1(w + c) : 1.0f, bs[e], &a[e], &s[e]);
             if (kPre) {
                 a[e] *= kGeluWScale;
                 s[e] *= kGeluWScale;
@@ -325,7 +345,7 @@ bn_col_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, cons
 #pragma unroll
                     for (int e = 0; e < V; ++e) {
                         if (ACT != kActNone) {
-                            float z = fmaf(xf[e], a[e], s[e]);
+                            float z = bn_pre<T>(xf[e], a[e], s[e], mean[e], bs[e]);
                             if (RES) z += rf[e];
                             dz[e] = df[e] * (kPre ? gelu_grad_fast_w(z) : act_grad_any<ACT, kFast>(z, act_rt, act_p));
                         } else {
@@ -441,7 +461,7 @@ bn_col_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
     const ColPos p = col_pos(g, V);
     const bool sc1_ok = col_sc1_ok<T>(g);
     if (!p.active) return;  // no barriers in this kernel
-    float k1[V], k2[V], k3[V], mean[V], a[V], s[V];
+    float k1[V], k2[V], k3[V], mean[V], a[V], s[V], bs[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
         const int64_t c = (p.col0 + e) / g.HW;
@@ -450,8 +470,8 @@ bn_col_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
         k3[e] = kExact ? coef[c * 4 + 2] : coef[c * 4 + 3];
         mean[e] = save_mean[c];
         a[e] = s[e] = 0.0f;
-        if (DZ_SRC == 2)
-            bn_coeffs(mean[e], save_rstd[c], w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a[e], &s[e]);
+        bs[e] = b ? ld1(b + c) : 0.0f;
+        if (DZ_SRC == 2) bn_coeffs(mean[e], save_rstd[c], w ? ld1(w + c) : 1.0f, bs[e], &a[e], &s[e]);
         if (kPre) {
             a[e] *= kGeluWScale;
             s[e] *= kGeluWScale;
@@ -483,7 +503,7 @@ bn_col_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
                 for (int e = 0; e < V; ++e) {
                     float dz = df[e];
                     if (DZ_SRC == 2 && ACT != kActNone) {
-                        float z = fmaf(xf[e], a[e], s[e]);
+                        float z = bn_pre<T>(xf[e], a[e], s[e], mean[e], bs[e]);
                         if (RES) z += rf[e];
                         dz = df[e] * (kPre ? gelu_grad_fast_w(z) : act_grad_any<ACT, kFast>(z, act_rt, act_p));
                     }

@@ -59,6 +59,19 @@ __device__ __forceinline__ void bn_coeffs(float mean, float rstd, float w, float
     *s = fmaf(-mean, *a, b);
 }
 
+// Pre-activation z = (x - mean) * a + b with a = w * rstd.  Float32 I/O forms
+// it centred, so a channel whose mean lies far from zero relative to its
+// spread keeps full precision (the folded form cancels two products of size
+// |mean| * a); 16-bit I/O, whose inputs cannot resolve such a channel anyway,
+// uses z = x * a + s with s = b - mean * a (one operation fewer).
+template <typename T>
+__device__ __forceinline__ float bn_pre(float x, float a, float s, float mean, float bias) {
+    if constexpr (sizeof(T) == 4)
+        return fmaf(x - mean, a, bias);
+    else
+        return fmaf(x, a, s);
+}
+
 // ------------------------------------------------------ pairwise statistics
 struct WelfF {
     float n, mean, m2;

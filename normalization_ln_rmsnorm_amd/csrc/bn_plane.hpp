@@ -96,6 +96,27 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, double *__restrict__ part) {
     // 2048 16-bit values per thread (a single 4 GiB plane is one tile).
     // Shorter planes keep the float32 state and wave merge throughout.
     const bool long_plane = nvp > kBnStatsChunk;  // the same in every lane
+    // Float32 I/O: when the tile's first vector shows a mean more than four
+    // of its own spreads from zero, values are folded relative to that mean,
+    // so the float32 state's rounding scales with the channel's spread
+    // rather than its mean.  Otherwise (and for 16-bit I/O) no shift: moving
+    // the origin by a value a few spreads from a near-zero mean would make
+    // the rounding larger, not smaller.  Every lane computes the same shift.
+    float shift = 0.0f;
+    if constexpr (sizeof(T) == 4 && V > 1) {  // one value has no spread to compare
+        if (nvp > 0) {
+            float f0[V];
+            VT::unpack(vload<T, V>(x + plane_offset(g, n0, c)), f0);
+            float s0 = 0.0f;
+#pragma unroll
+            for (int e = 0; e < V; ++e) s0 += f0[e];
+            const float m0 = s0 * (1.0f / V);
+            float q0 = 0.0f;
+#pragma unroll
+            for (int e = 0; e < V; ++e) q0 = fmaf(f0[e] - m0, f0[e] - m0, q0);
+            if (m0 * m0 > 16.0f * (q0 * (1.0f / V))) shift = m0;
+        }
+    }
     WelfF st{0.0f, 0.0f, 0.0f};
     WelfD acc{0.0, 0.0, 0.0};
     for (int64_t n = n0; n < n1; ++n) {
@@ -115,6 +136,8 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, double *__restrict__ part) {
                     if (v < ve) {
                         float f[V];
                         VT::unpack(r[u], f);
+#pragma unroll
+                        for (int e = 0; e < V; ++e) f[e] -= shift;
                         float s = 0.0f;
 #pragma unroll
                         for (int e = 0; e < V; ++e) s += f[e];
@@ -130,7 +153,7 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, double *__restrict__ part) {
                 }
             }
             if (long_plane) {
-                acc = welf_merge(acc, WelfD{st.n, st.mean, st.m2});
+                acc = welf_merge(acc, WelfD{st.n, (double)st.mean + shift, st.m2});
                 st = WelfF{0.0f, 0.0f, 0.0f};
             }
         }
@@ -139,7 +162,7 @@ bn_stats_kernel(const T *__restrict__ x, BnGeom g, double *__restrict__ part) {
         acc = wave_merge(acc);
     } else {
         st = wave_merge(st);
-        acc = WelfD{st.n, st.mean, st.m2};
+        acc = WelfD{st.n, (double)st.mean + shift, st.m2};
     }
 
     __shared__ WelfD wave_part[kBnWaves];
@@ -247,7 +270,8 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
         rstd = 1.0f / sqrtf(running_var[c] + eps);
     }
     float a, s;
-    bn_coeffs(mean, rstd, w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a, &s);
+    const float bias = b ? ld1(b + c) : 0.0f;
+    bn_coeffs(mean, rstd, w ? ld1(w + c) : 1.0f, bias, &a, &s);
     const int64_t nvp = g.HW / V;
     const bool sc1_ok = plane_sc1_ok<T>(g);
     // Vectors in flight per thread: 8, or 4 for the 16-bit training apply
@@ -276,7 +300,7 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
                     if (RES) VT::unpack(rr[u], rf);
 #pragma unroll
                     for (int e = 0; e < V; ++e) {
-                        float z = fmaf(f[e], a, s);
+                        float z = bn_pre<T>(f[e], a, s, mean, bias);
                         if (RES) z += rf[e];
                         o[e] = act_fwd_io<T, ACT>(z, act_rt, act_p);
                     }
@@ -301,7 +325,8 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
     tile_of_block(g, &c, &n0, &n1);
     const float mean = save_mean[c];
     float a, s;
-    bn_coeffs(mean, save_rstd[c], w ? ld1(w + c) : 1.0f, b ? ld1(b + c) : 0.0f, &a, &s);
+    const float bias = b ? ld1(b + c) : 0.0f;
+    bn_coeffs(mean, save_rstd[c], w ? ld1(w + c) : 1.0f, bias, &a, &s);
     constexpr bool kPre = kGeluPrescale<T, ACT, RES>;
     if (kPre) {
         a *= kGeluWScale;
@@ -353,7 +378,7 @@ bn_bwd_reduce_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T 
 #pragma unroll
                     for (int e = 0; e < V; ++e) {
                         if (ACT != kActNone) {
-                            float z = fmaf(xf[e], a, s);
+                            float z = bn_pre<T>(xf[e], a, s, mean, bias);
                             if (RES) z += rf[e];
                             dz[e] = df[e] * (kPre ? gelu_grad_fast_w(z)
                                                   : act_grad_any<ACT, kFastGrad<T>>(z, act_rt, act_p));
@@ -465,7 +490,8 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
     constexpr bool kExact = sizeof(T) == 4;
     const float k3m = kc.k3m;
     float a = 0.0f, s = 0.0f;
-    if (DZ_SRC == 2) bn_coeffs(mean, rstd_f, wc_f, b ? ld1(b + c) : 0.0f, &a, &s);
+    const float bias = b ? ld1(b + c) : 0.0f;
+    if (DZ_SRC == 2) bn_coeffs(mean, rstd_f, wc_f, bias, &a, &s);
     constexpr bool kPre = kGeluPrescale<T, ACT, RES>;
     if (kPre) {
         a *= kGeluWScale;
@@ -500,7 +526,7 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
                     for (int e = 0; e < V; ++e) {
                         float dz = df[e];
                         if (DZ_SRC == 2 && ACT != kActNone) {
-                            float z = fmaf(xf[e], a, s);
+                            float z = bn_pre<T>(xf[e], a, s, mean, bias);
                             if (RES) z += rf[e];
                             dz = df[e] * (kPre ? gelu_grad_fast_w(z) : act_grad_any<ACT, kFast>(z, act_rt, act_p));
                         }

@@ -345,3 +345,24 @@ def test_long_planes(orc, dtype):
     HW = (1 << 21) + 512
     print(f"case bn long planes {dtype} 2x3x{HW}", flush=True)
     run_case(orc, dtype, 2, 3, HW, "gelu", True)
+
+
+@pytest.mark.parametrize("path", ["plane", "cols"])
+@pytest.mark.parametrize("act,residual", [("relu", True), ("gelu", False)])
+def test_f32_channels_far_from_zero(orc, monkeypatch, path, act, residual):
+    """float32 channels whose mean is up to ~50 spreads from zero: the
+    recipe's channels moved by a per-channel offset of 10-25 (either sign).
+    The statistics fold values relative to a per-tile shift and the
+    pre-activation is formed centred, so the 1e-5 tolerance holds.  The
+    float32 saved mean, from which the backward recomputes z, bounds the
+    range: its rounding moves every z of the channel alike, and with GELU
+    db (a sum of n derivatives) reaches the tolerance near |mean| / std ~
+    100."""
+    monkeypatch.setenv("MI355NORM_BN_PATH", path)
+    Nb, C, HW = (4, 8, 3136) if path == "plane" else (256, 64, 1)
+    inp = gen_bn(_wl("f32", act, residual), Nb=Nb, C=C, HW=HW)
+    rng = np.random.default_rng(777)
+    off = rng.uniform(10.0, 25.0, C) * rng.choice([-1.0, 1.0], C)
+    inp["x"] = (inp["x"].astype(np.float64) + off[None, :, None]).astype(np.float32)
+    print(f"case bn f32 far-from-zero path={path} {Nb}x{C}x{HW} {act} res={residual}", flush=True)
+    run_case(orc, "f32", Nb, C, HW, act, residual, inp=inp)
