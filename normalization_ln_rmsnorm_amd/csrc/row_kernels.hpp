@@ -156,15 +156,31 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
 
         float mean = 0.0f;
         if (!RMS) {
+            // Float32 I/O sums the row relative to its first element, so a
+            // row far from zero relative to its spread keeps its mean's
+            // precision (16-bit inputs cannot resolve such a row).
+            float x0 = 0.0f;
+            if constexpr (sizeof(T) == 4) {
+                if (active) x0 = ld1(x + row * N);
+            }
             float s = 0.0f;
 #pragma unroll
             for (int k = 0; k < IT; ++k) {
                 float f[V];
                 VT::unpack(xr[k], f);
+                if constexpr (sizeof(T) == 4) {
+                    const bool valid = lane + k * tpr < nv;  // out-of-range slots hold 0, not x0
 #pragma unroll
-                for (int e = 0; e < V; ++e) s += f[e];
+                    for (int e = 0; e < V; ++e) s += valid ? f[e] - x0 : 0.0f;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < V; ++e) s += f[e];
+                }
             }
-            mean = row_sum(s, tpr, lds, 0) * inv_n;
+            if constexpr (sizeof(T) == 4)
+                mean = x0 + row_sum(s, tpr, lds, 0) * inv_n;
+            else
+                mean = row_sum(s, tpr, lds, 0) * inv_n;
 #pragma unroll
             for (int k = 0; k < IT; ++k) opaque(xr[k]);
         }
@@ -227,6 +243,7 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
     __shared__ float lds[2][kMaxWavesPerBlock][2];
+    __shared__ float lds_c[2][kMaxWavesPerBlock];  // float32 LayerNorm: the mean correction
 
     const int nv = N / V;
     const int lane = threadIdx.x & (tpr - 1);
@@ -255,7 +272,7 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
     // (clamped) loads that keep the next row in flight through the passes
     // measured slower on the RMSNorm 16384 x 4096 backward: more reads in
     // flight per CU lower this two-read, one-write pass's bandwidth.
-    int slot = 0;
+    int slot = 0, slot_c = 0;
     const int64_t step = (int64_t)gridDim.x * rpb;
     int64_t base = (int64_t)blockIdx.x * rpb;
     raw_t rx[IT], rd[IT];
@@ -309,6 +326,29 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
 #pragma unroll
         for (int k = 0; k < IT; ++k) opaque(wr[k]);  // keep w packed (no hoisted float copy)
 
+        // Float32 LayerNorm: the saved mean is the float32 rounding of the
+        // row mean, an error shared by every element of the row that would
+        // add coherently into dw.  One more row sum, of x - mean, gives the
+        // exact mean as mean + corr (kept in two parts: x - mean is exact for
+        // x near the mean, corr is small), as the BatchNorm backward does
+        // with its channel sums.  16-bit I/O: corr = 0.
+        float corr = 0.0f;
+        if constexpr (sizeof(T) == 4 && !RMS) {
+            float sc = 0.0f;
+#pragma unroll
+            for (int k = 0; k < IT; ++k) {
+                const bool valid = lane + k * tpr < nv;
+                float xf[V];
+                VT::unpack(rx[k], xf);
+#pragma unroll
+                for (int e = 0; e < V; ++e) sc += valid ? xf[e] - mean : 0.0f;
+            }
+            corr = row_sum(sc, tpr, lds_c, slot_c) * inv_n;
+            slot_c ^= 1;
+#pragma unroll
+            for (int k = 0; k < IT; ++k) opaque(rx[k]);
+        }
+
         // Pass 1: the row sums and the column partials.  Out-of-range
         // elements hold x = dy = 0 and add nothing (their g is 0).  g is
         // kept in float32 for pass 2, which then needs neither dy nor w.
@@ -322,7 +362,9 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
             VT::unpack(wr[k], wf);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                const float xh = (RMS ? xf[e] : xf[e] - mean) * rstd;
+                float xc = RMS ? xf[e] : xf[e] - mean;
+                if constexpr (sizeof(T) == 4 && !RMS) xc -= corr;
+                const float xh = xc * rstd;
                 acc_w[k][e] = fmaf(df[e], xh, acc_w[k][e]);
                 if (!RMS) acc_b[k][e] += df[e];
                 const float g = df[e] * wf[e];
@@ -338,7 +380,8 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
         // element after the centring subtraction (none for RMSNorm).
         const float c_gx = s_gx * inv_n, c_g = s_g * inv_n;
         const float k1 = -(rstd * rstd) * c_gx;
-        const float k0 = -rstd * c_g;
+        float k0 = -rstd * c_g;
+        if constexpr (sizeof(T) == 4 && !RMS) k0 = fmaf(-k1, corr, k0);  // (x - mean - corr) k1 + k0
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             opaque(rx[k]);

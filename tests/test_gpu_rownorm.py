@@ -43,10 +43,11 @@ def _wl(kind, dtype):
 
 
 def run_case(orc, kind, dtype, M, N, with_w=True, with_b=True, eps=None, seed=None, guard=True,
-             report=None):
+             report=None, inp=None):
     wl = _wl(kind, dtype)
     eps = wl.eps if eps is None else eps
-    inp = gen_rowwise(wl, M=M, N=N, seed=seed)
+    if inp is None:
+        inp = gen_rowwise(wl, M=M, N=N, seed=seed)
     bf16 = dtype == "bf16"
     tdt = TORCH_DTYPE[dtype]
     x = to_dev(inp["x"], dtype)
@@ -263,3 +264,19 @@ def test_rows_past_2_32_elements(orc, kind):
     check(f"{tag} dw / copies", to_f64(dw) / reps, rdw, dtype)
     if kind == "ln":
         check(f"{tag} db / copies", to_f64(db) / reps, rdb, dtype)
+
+
+@pytest.mark.parametrize("M,N", [(64, 256), (37, 768), (17, 4096)])
+def test_f32_rows_far_from_zero(orc, M, N):
+    """float32 LayerNorm rows moved by a per-row offset of 50-100 (either
+    sign; the recipe's rows have spread ~1).  The row is summed relative to
+    its first element, then centred exactly in registers, so the 1e-5
+    tolerance holds; the float32 saved mean, from which the backward forms
+    xhat, bounds the range near |mean| / std ~ 300."""
+    wl = _wl("ln", "f32")
+    inp = gen_rowwise(wl, M=M, N=N)
+    rng = np.random.default_rng(4242)
+    off = rng.uniform(50.0, 100.0, M) * rng.choice([-1.0, 1.0], M)
+    inp["x"] = (inp["x"].astype(np.float64) + off[:, None]).astype(np.float32)
+    print(f"case ln f32 far-from-zero {M}x{N}", flush=True)
+    run_case(orc, "ln", "f32", M, N, inp=inp)
