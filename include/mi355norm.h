@@ -31,8 +31,10 @@
  *   Kernels are enqueued on it and the call returns without synchronizing.
  * Ownership.  The caller allocates and owns every buffer, including the
  *   workspace; the library never allocates, frees or synchronizes, and keeps
- *   no state between calls.  Concurrent calls are safe if they use distinct
- *   output and workspace buffers.  Outputs must not alias inputs.
+ *   no state between calls (apart from the process-wide test hook
+ *   norm_bn_force_path and the per-thread timing hook below).  Concurrent
+ *   calls are safe if they use distinct output and workspace buffers.
+ *   Outputs must not alias inputs.
  * Capture.  A call enqueues kernels only (no memset, copy or host wait), so
  *   it can be recorded into a HIP graph by stream capture and replayed; the
  *   pointers and sizes are fixed at capture, as for any captured launch.
@@ -40,8 +42,11 @@
  *   on the host before anything is enqueued; on an error nothing is
  *   launched and no output is touched.  A zero-sized problem (M == 0, or
  *   C == 0 / Nb*HW == 0 for BatchNorm eval) is a successful no-op.  A
- *   failed launch returns NORM_ERR_HIP.  Faults inside a kernel surface at
- *   the caller's next synchronization, as for any stream operation.
+ *   launch the HIP runtime rejects returns NORM_ERR_HIP; the status comes
+ *   from the call's own launches (the thread's sticky HIP error, which may
+ *   hold an earlier failure of the caller's, is neither read nor cleared).
+ *   Faults inside a kernel surface at the caller's next synchronization, as
+ *   for any stream operation.
  */
 #ifndef MI355NORM_H
 #define MI355NORM_H
@@ -254,6 +259,18 @@ void norm_arm_kernel_events(void *const *events, int n_pairs);
 int norm_last_kernel_count(void);
 const char *norm_last_kernel_name(int i);
 int norm_last_main_kernel(void);
+
+/* Test hook: pins BatchNorm's data path for every later call in this
+ * process.  0 = automatic (chosen from dt, C and HW), 1 = the plane path
+ * (workgroups stream whole (n, c) planes), 2 = the column path (workgroups
+ * stream a band of columns down the samples).  Both paths compute the same
+ * results; the hook lets a test run either on any shape.
+ * bn_workspace_bytes follows the setting, so set it before querying the
+ * workspace and keep it until the calls that use that workspace have been
+ * enqueued (a call given a workspace sized for the other path returns
+ * NORM_ERR_WORKSPACE if it is too small).  Returns the previous setting,
+ * or -1 (and changes nothing) for any other value.                       */
+int norm_bn_force_path(int path);
 
 #ifdef __cplusplus
 }

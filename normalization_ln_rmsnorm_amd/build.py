@@ -35,22 +35,31 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
          "-I" + os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, tuning: bool = False, out: str = None) -> str:
+    """Compile and link the library.  tuning=True defines MI355NORM_TUNING,
+    which compiles in the environment overrides of the launch plans used by
+    tuning sweeps (the regular library has none); such a build goes to
+    `out`, never over the regular library."""
+    if tuning and not out:
+        raise ValueError("a tuning build needs its own output path")
+    out = out or OUT
+    build_dir = BUILD + ("_tuning" if tuning else "")
+    os.makedirs(build_dir, exist_ok=True)
     t0 = time.time()
     procs = []
     objs = []
     for src, name, extra in SOURCES:
-        obj = os.path.join(BUILD, name + ".o")
+        obj = os.path.join(build_dir, name + ".o")
         objs.append(obj)
-        cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *(["-DMI355NORM_TUNING"] if tuning else []), *extra, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((name, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     failed = []
     for src, p in procs:
-        out, _ = p.communicate()
-        text = "\n".join(l for l in out.decode(errors="replace").splitlines()
+        log, _ = p.communicate()
+        text = "\n".join(l for l in log.decode(errors="replace").splitlines()
                          if "packed-fp32-ops" not in l)
         if p.returncode != 0:
             failed.append(src)
@@ -59,15 +68,15 @@ def build(verbose: bool = False) -> str:
             print(text)
     if failed:
         raise RuntimeError("HIP compile failed: " + ", ".join(failed))
-    tmp = OUT + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT} in {time.time() - t0:.1f}s", flush=True)
-    return OUT
+        print(f"built {out} in {time.time() - t0:.1f}s", flush=True)
+    return out
 
 
 if __name__ == "__main__":

@@ -15,6 +15,7 @@ struct CallState {
     int armed_pairs = 0;           // pairs armed for the current / next call
     int count = 0;                 // kernels launched by the current / last call
     int main_index = -1;
+    bool launch_failed = false;    // a launch of the current call was rejected
     const char *names[kMaxKernelsPerCall] = {};
 };
 thread_local CallState g_call;
@@ -39,7 +40,14 @@ int device_cu_count() {
 void call_begin() {
     g_call.count = 0;
     g_call.main_index = -1;
+    g_call.launch_failed = false;
 }
+
+void note_launch(hipError_t rc) {
+    if (rc != hipSuccess) g_call.launch_failed = true;
+}
+
+bool call_launch_failed() { return g_call.launch_failed; }
 
 void call_end() { g_call.armed_pairs = 0; }
 

@@ -22,16 +22,20 @@
 //   column path   otherwise, when a sample's C * HW values split into
 //                 128-bit vectors (or the planes are short anyway): each
 //                 workgroup streams a band of columns down the samples.
-// MI355NORM_BN_PATH=plane|cols forces one (tests of both paths on the same
-// shapes) and MI355NORM_BN_COL_PLAN="rows_per_tile,vectors_per_row_slice"
-// overrides the column tiling (tuning sweeps); both are read per call, like
-// MI355NORM_BN_TILE, so the workspace query and the call must see the same.
+// norm_bn_force_path() pins one path for the whole process (tests of both
+// paths on the same shapes); the workspace query follows it.  A library
+// built with -DMI355NORM_TUNING also reads MI355NORM_BN_TILE (plane-path
+// values per workgroup) and MI355NORM_BN_COL_PLAN ("rows_per_tile,
+// vectors_per_row_slice"), once per process, for tuning sweeps; the regular
+// build has no run-time knobs.
 #include <hip/hip_runtime.h>
 
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <utility>
 #include <initializer_list>
 
 #include "bn_common.hpp"
@@ -48,11 +52,14 @@ enum BnPath { kPathPlane = 0, kPathCols = 1 };
 // 16-bit values, rounded up to whole planes), the best of a sweep over the
 // two BatchNorm2d workloads.  MI355NORM_BN_TILE (values) overrides it.
 static int64_t tile_elems(norm_dtype dt) {
-    const char *e = getenv("MI355NORM_BN_TILE");
-    if (e && *e) {
-        const long long v = atoll(e);
-        if (v >= 256 && v <= (1LL << 26)) return v;
-    }
+#ifdef MI355NORM_TUNING
+    static const long long over = [] {
+        const char *e = getenv("MI355NORM_BN_TILE");
+        const long long v = (e && *e) ? atoll(e) : 0;
+        return (v >= 256 && v <= (1LL << 26)) ? v : 0;
+    }();
+    if (over) return over;
+#endif
     return kBnTileBytes / (int64_t)dtype_size(dt);
 }
 
@@ -69,10 +76,13 @@ static BnGeom make_geom(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW) {
     return g;
 }
 
+// 0: automatic; 1: plane path; 2: column path (norm_bn_force_path).
+static std::atomic<int> g_forced_path{0};
+
 static BnPath choose_path(norm_dtype dt, int64_t C, int64_t HW) {
-    const char *e = getenv("MI355NORM_BN_PATH");
-    if (e && strcmp(e, "plane") == 0) return kPathPlane;
-    if (e && strcmp(e, "cols") == 0) return kPathCols;
+    const int forced = g_forced_path.load(std::memory_order_relaxed);
+    if (forced == 1) return kPathPlane;
+    if (forced == 2) return kPathCols;
     const int64_t es = (int64_t)dtype_size(dt), v = 16 / es;
     const bool long_plane = HW * es >= kBnPlaneMinBytes;
     if (long_plane && HW % v == 0) return kPathPlane;
@@ -95,11 +105,19 @@ static BnColGeom make_col_geom(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW,
     g.K = C * HW;
     g.KV = g.K / V;
     int ov_rt = 0, ov_cv = 0;
-    const char *e = getenv("MI355NORM_BN_COL_PLAN");
-    if (e && *e && sscanf(e, "%d,%d", &ov_rt, &ov_cv) == 2) {
-        if (ov_rt < 1 || ov_rt > (1 << 20)) ov_rt = 0;
-        if (ov_cv != 16 && ov_cv != 32 && ov_cv != 64 && ov_cv != 128 && ov_cv != 256) ov_cv = 0;
-    }
+#ifdef MI355NORM_TUNING
+    static const std::pair<int, int> over = [] {
+        int rt = 0, cv = 0;
+        const char *e = getenv("MI355NORM_BN_COL_PLAN");
+        if (e && *e && sscanf(e, "%d,%d", &rt, &cv) == 2) {
+            if (rt < 1 || rt > (1 << 20)) rt = 0;
+            if (cv != 16 && cv != 32 && cv != 64 && cv != 128 && cv != 256) cv = 0;
+        }
+        return std::make_pair(rt, cv);
+    }();
+    ov_rt = over.first;
+    ov_cv = over.second;
+#endif
     const int64_t cv_max = ov_cv ? ov_cv : kWave;
     g.CV = (int)(g.KV < cv_max ? (g.KV > 0 ? g.KV : 1) : cv_max);
     g.RPP = kBnBlock / g.CV;
@@ -250,4 +268,9 @@ extern "C" norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, 
     a.sm = const_cast<float *>(save_mean); a.sr = const_cast<float *>(save_rstd);
     a.dx = dx; a.dres = dres; a.dw = dw; a.db = db; a.ws = ws;
     return run(dt, Nb, C, HW, kOpBwd, a, {dy, x, res, dx, dres});
+}
+
+extern "C" int norm_bn_force_path(int path) {
+    if (path < 0 || path > 2) return -1;
+    return g_forced_path.exchange(path);
 }

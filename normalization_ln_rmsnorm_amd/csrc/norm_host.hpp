@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+
 #include "../../include/mi355norm.h"
 #include "norm_device.hpp"
 
@@ -34,30 +36,46 @@ int device_cu_count();
 
 // Per-call kernel bookkeeping behind norm_arm_kernel_events: every entry
 // point opens a CallScope; every kernel goes through launch(), which
-// attaches the armed event pair (if any) to that kernel's dispatch.
+// attaches the armed event pair (if any) to that kernel's dispatch and
+// records whether the runtime accepted the launch.
 void call_begin();
 void call_end();
 bool kernel_events(const char *name, bool is_main, hipEvent_t *start, hipEvent_t *stop);
+void note_launch(hipError_t rc);
+bool call_launch_failed();
 
 struct CallScope {
     CallScope() { call_begin(); }
     ~CallScope() { call_end(); }
 };
 
-template <typename F, typename... Args>
-inline void launch(const char *name, bool is_main, F fn, dim3 grid, dim3 block, size_t shmem,
-                   hipStream_t s, Args... args) {
+// Enqueues fn<<<grid, block, shmem, s>>>(args...).  The arguments are
+// converted to the kernel's own parameter types first (the runtime copies
+// them by address), and the launch's own return code is kept for this
+// call's status: the thread's sticky last error, which may hold a failure
+// of something the caller did earlier, is neither read nor cleared.
+template <typename... P, typename... A>
+inline void launch(const char *name, bool is_main, void (*fn)(P...), dim3 grid, dim3 block, size_t shmem,
+                   hipStream_t s, A... args) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    std::tuple<P...> conv(static_cast<P>(args)...);
+    void *argv[sizeof...(P) > 0 ? sizeof...(P) : 1] = {};
+    std::apply([&argv](auto &...a) {
+        int i = 0;
+        ((argv[i++] = static_cast<void *>(&a)), ...);
+    }, conv);
     hipEvent_t e0 = nullptr, e1 = nullptr;
+    const void *f = reinterpret_cast<const void *>(fn);
+    hipError_t rc;
     if (kernel_events(name, is_main, &e0, &e1))
-        hipExtLaunchKernelGGL(fn, grid, block, (uint32_t)shmem, s, e0, e1, 0u, args...);
+        rc = hipExtLaunchKernel(f, grid, block, argv, shmem, s, e0, e1, 0);
     else
-        hipLaunchKernelGGL(fn, grid, block, shmem, s, args...);
+        rc = hipLaunchKernel(f, grid, block, argv, shmem, s);
+    note_launch(rc);
 }
 
-// Map the launch status of the kernels just enqueued.
-inline norm_status launch_status() {
-    return hipGetLastError() == hipSuccess ? NORM_OK : NORM_ERR_HIP;
-}
+// Status of the kernels this call has enqueued so far.
+inline norm_status launch_status() { return call_launch_failed() ? NORM_ERR_HIP : NORM_OK; }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

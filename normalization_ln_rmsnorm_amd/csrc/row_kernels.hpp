@@ -127,6 +127,13 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
     // compiler waits for all outstanding loads before the row's first pass.
     const int64_t step = (int64_t)gridDim.x * rpb;
     int64_t base = (int64_t)blockIdx.x * rpb;
+    // LDS slot of the sum of squares.  A row spanning several waves reads
+    // every wave's partial after one barrier; a fast wave may reach the next
+    // row's write before a slow one has read this row's partials, so two
+    // consecutive reductions never use the same slot: LayerNorm takes slot 0
+    // (mean) then 1 (squares) in every row, RMSNorm alternates its single
+    // reduction between the slots from row to row.
+    int qslot = 1;
     raw_t xr[IT];
     {
         const int64_t row = base + slot_in_block;
@@ -196,7 +203,8 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
                 q += valid ? d * d : 0.0f;
             }
         }
-        const float rstd = rsqrtf(row_sum(q, tpr, lds, 1) * inv_n + eps);
+        const float rstd = rsqrtf(row_sum(q, tpr, lds, qslot) * inv_n + eps);
+        if (RMS) qslot ^= 1;
 #pragma unroll
         for (int k = 0; k < IT; ++k) opaque(xr[k]);
 

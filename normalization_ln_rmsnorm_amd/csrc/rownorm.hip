@@ -25,16 +25,26 @@ constexpr int64_t kDirectRowGroups = 8;  // backward: one block (no column-sum k
 static const int kVecIts[] = {1, 2, 3, 4, 6, 8};
 static const int kScalarIts[] = {1, 2, 4, 8, 16, 32, 64};
 
-// Optional tuning override for experiments:
-// MI355NORM_ROW_PLAN="tpr,it,blocks_per_cu[,block_threads]".
+// Tuning override for sweeps, compiled only into a library built with
+// -DMI355NORM_TUNING (the regular build has no run-time knobs):
+// MI355NORM_ROW_PLAN="tpr,it,blocks_per_cu[,block_threads]", read once per
+// process.
 static bool env_override(int *tpr, int *it, int *bpc, int *block) {
-    const char *s = getenv("MI355NORM_ROW_PLAN");
-    if (!s || !*s) return false;
-    int a = 0, b = 0, c = 0, d = 0;
-    const int n = sscanf(s, "%d,%d,%d,%d", &a, &b, &c, &d);
-    if (n < 3) return false;
-    *tpr = a; *it = b; *bpc = c; *block = n == 4 ? d : 0;
+#ifdef MI355NORM_TUNING
+    static const struct Parsed {
+        int n = 0, a = 0, b = 0, c = 0, d = 0;
+        Parsed() {
+            const char *s = getenv("MI355NORM_ROW_PLAN");
+            if (s && *s) n = sscanf(s, "%d,%d,%d,%d", &a, &b, &c, &d);
+        }
+    } plan;
+    if (plan.n < 3) return false;
+    *tpr = plan.a; *it = plan.b; *bpc = plan.c; *block = plan.n == 4 ? plan.d : 0;
     return true;
+#else
+    (void)tpr; (void)it; (void)bpc; (void)block;
+    return false;
+#endif
 }
 
 static bool make_plan(norm_dtype dt, int64_t M, int64_t N, bool vec_ok, bool backward, RowPlan *p) {

@@ -52,6 +52,7 @@ SIGNATURES = {
     "norm_last_kernel_count": (_I, []),
     "norm_last_kernel_name": (ctypes.c_char_p, [_I]),
     "norm_last_main_kernel": (_I, []),
+    "norm_bn_force_path": (_I, [_I]),
 }
 
 _lib = None
@@ -140,6 +141,17 @@ def arm_kernel_events(events):
     arr = (ctypes.c_void_p * len(events))(
         *[ctypes.c_void_p(None if e is None else getattr(e, "value", e)) for e in events])
     lib().norm_arm_kernel_events(arr, len(events) // 2)
+
+
+BN_PATHS = {"auto": 0, "plane": 1, "cols": 2}
+
+
+def bn_force_path(path):
+    """Pin BatchNorm's data path ("auto", "plane" or "cols") for every later
+    call in this process; returns the previous setting's name (a test hook:
+    both paths compute the same results)."""
+    prev = lib().norm_bn_force_path(BN_PATHS[path])
+    return {v: k for k, v in BN_PATHS.items()}[prev]
 
 
 def last_kernels():

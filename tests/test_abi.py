@@ -176,3 +176,29 @@ def test_act_dropout_errors(lib):
     assert lib.act_dropout_bwd(F32, 16, 0, 0.0, 0.5, 1, 0, P, NULL, P, NULL) == ENULL
     assert lib.act_dropout_bwd(F32, 16, 0, 0.0, 0.5, 1, 6, P, P, P, NULL) == EARG
     assert lib.act_dropout_bwd(BF16, 0, 0, 0.0, 0.5, 1, 0, NULL, NULL, NULL, NULL) == OK
+
+
+def test_bn_force_path_hook(lib):
+    """The test hook pins the data path; the workspace query follows it, and
+    invalid settings are refused without a change."""
+    lib.norm_bn_force_path.restype = ctypes.c_int
+    lib.norm_bn_force_path.argtypes = [ctypes.c_int]
+    auto = lib.bn_workspace_bytes(BF16, 256, 64, 12544)
+    assert lib.norm_bn_force_path(1) == 0
+    plane = lib.bn_workspace_bytes(BF16, 256, 64, 12544)
+    assert lib.norm_bn_force_path(2) == 1
+    cols = lib.bn_workspace_bytes(BF16, 256, 64, 12544)
+    assert lib.norm_bn_force_path(3) == -1 and lib.norm_bn_force_path(-1) == -1
+    assert lib.norm_bn_force_path(0) == 2
+    assert auto == plane and cols != plane and cols > 0
+    assert lib.bn_workspace_bytes(BF16, 256, 64, 12544) == auto
+
+
+def test_regular_build_reads_no_environment():
+    """The shipped library has no run-time tuning knobs: it does not import
+    getenv (tuning sweeps use a separate build with -DMI355NORM_TUNING)."""
+    from normalization_ln_rmsnorm_amd import normlib
+    out = subprocess.run(["nm", "-D", "--undefined-only", normlib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    imported = set(line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip())
+    assert "getenv" not in imported and "secure_getenv" not in imported
