@@ -20,9 +20,12 @@ call are recorded too (they add the ~6 us dispatch latency of a lone launch).
 
 Bytes are algorithmic: what the method must move (every activation tensor in
 its I/O dtype once per pass that touches it, plus the small vectors), not
-what the hardware happened to move.  The default workload is RMSNorm bf16
-16384 x 4096; the other workloads are measured too and reported under
-"per_workload".  Rank 0 prints one JSON line.
+what the hardware happened to move.  The default workload is the largest:
+BatchNorm2d bf16 256 x 64 x 112 x 112 with exact GELU (training forward,
+backward, eval forward); the other workloads are measured too and reported
+under "per_workload", each with the float64 oracle timed on the host cores
+beside it.  `value` is the whole step's algorithmic bytes over its summed
+device time.  Rank 0 prints one JSON line.
 """
 import argparse
 import ctypes
@@ -51,7 +54,10 @@ def parse():
     p.add_argument("--no-others", action="store_true", help="skip the other workloads")
     p.add_argument("--other-steps", type=int, default=20)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="oracle time spent on the headline workload's CPU baseline")
+    p.add_argument("--other-cpu-seconds", type=float, default=2.0,
+                   help="oracle time spent on each other workload's CPU baseline")
     p.add_argument("--flush", choices=["read", "write"], default="read",
                    help="evict the caches by reading (default) or rewriting a 512 MiB buffer")
     return p.parse_args()
@@ -175,6 +181,17 @@ class RowBench:
             else:
                 nl.rms_bwd(self.dy, self.x, self.w, self.rstd, dx=self.dx, dw=self.dw, ws=self.ws)
 
+    def cpu_units(self):
+        """Rows: the oracle is timed on groups of whole rows."""
+        return self.wl.shape[0]
+
+    def cpu_prepare(self, orc, r0, r1):
+        bf16 = self.wl.dtype == "bf16"
+        inp = self.inp
+        return dict(x=orc.widen(inp["x"][r0:r1], bf16=bf16), dy=orc.widen(inp["dy"][r0:r1], bf16=bf16),
+                    w=orc.widen(inp["w"], bf16=bf16),
+                    b=orc.widen(inp["b"], bf16=bf16) if inp["b"] is not None else None)
+
     def cpu_step(self, orc, arrays):
         wl = self.wl
         if wl.kind == "ln":
@@ -198,7 +215,7 @@ class BnBench:
         self.dy = dev(inp["dy"]).view(shape)
         self.res = dev(inp["res"]).view(shape) if wl.residual else None
         self.w, self.b = dev(inp["w"]), dev(inp["b"])
-        del inp
+        self.inp = inp  # host copy for the CPU oracle baseline
         self.rm = torch.zeros(C, device="cuda")
         self.rv = torch.ones(C, device="cuda")
         self.y = torch.empty(shape, dtype=tdt, device="cuda")
@@ -213,6 +230,31 @@ class BnBench:
         self.bytes = bytes_bn(wl, ELEM_SIZE[wl.dtype])
         self.ops = ["fwd", "bwd"] + (["eval"] if wl.eval_after_train else [])
         self.dominant = "bwd"
+
+    def cpu_units(self):
+        """Channels: the oracle is timed on groups of whole channels."""
+        return self.wl.shape[1]
+
+    def cpu_prepare(self, orc, c0, c1):
+        """float64 copies of channels c0..c1-1 (outside the timed region)."""
+        bf16 = self.wl.dtype == "bf16"
+        sub = lambda a: orc.widen(np.ascontiguousarray(a[:, c0:c1, :]), bf16=bf16)
+        inp = self.inp
+        return dict(x=sub(inp["x"]), dy=sub(inp["dy"]),
+                    res=sub(inp["res"]) if inp["res"] is not None else None,
+                    w=orc.widen(inp["w"][c0:c1], bf16=bf16), b=orc.widen(inp["b"][c0:c1], bf16=bf16),
+                    rm=inp["running_mean"][c0:c1].astype(np.float64),
+                    rv=inp["running_var"][c0:c1].astype(np.float64))
+
+    def cpu_step(self, orc, a):
+        """One step of the oracle on a group of channels: training forward
+        (statistics, EMA, activation), backward, and the eval forward."""
+        wl = self.wl
+        _, _, _, rm, rv = orc.bn_fwd_train(a["x"], a["res"], a["w"], a["b"], a["rm"], a["rv"],
+                                           eps=wl.eps, momentum=wl.momentum, act=wl.act)
+        orc.bn_bwd(a["dy"], a["x"], a["res"], a["w"], a["b"], eps=wl.eps, act=wl.act)
+        if wl.eval_after_train:
+            orc.bn_fwd_eval(a["x"], rm, rv, a["res"], a["w"], a["b"], eps=wl.eps, act=wl.act)
 
     def run(self, op):
         nl, wl = self.nl, self.wl
@@ -237,13 +279,28 @@ class AdBench:
         inp = gen_act_dropout(wl)
         self.x = to_device(torch, inp["x"], wl.dtype)
         self.dy = to_device(torch, inp["dy"], wl.dtype)
-        del inp
+        self.inp = inp  # host copy for the CPU oracle baseline
         self.y = torch.empty_like(self.x)
         self.dx = torch.empty_like(self.x)
         self.p, self.seed = wl.extra["drop_p"], wl.extra["dropout_seed"]
         self.bytes = bytes_act_dropout(wl, ELEM_SIZE[wl.dtype])
         self.ops = ["fwd", "bwd"]
         self.dominant = "bwd"
+
+    def cpu_units(self):
+        """Blocks of 2^16 elements (offsets stay multiples of 4)."""
+        return -(-self.x.numel() // (1 << 16))
+
+    def cpu_prepare(self, orc, u0, u1):
+        bf16 = self.wl.dtype == "bf16"
+        a, b = u0 << 16, min(u1 << 16, self.x.numel())
+        return dict(x=orc.widen(self.inp["x"][a:b], bf16=bf16),
+                    dy=orc.widen(self.inp["dy"][a:b], bf16=bf16), offset=a)
+
+    def cpu_step(self, orc, a):
+        wl = self.wl
+        orc.act_dropout_fwd(a["x"], wl.act, self.p, self.seed, a["offset"])
+        orc.act_dropout_bwd(a["dy"], a["x"], wl.act, self.p, self.seed, a["offset"])
 
     def run(self, op):
         nl, wl = self.nl, self.wl
@@ -374,6 +431,13 @@ def summarize(bench, meas):
     res["fwd_bwd"] = {"ms": tot_ms, "bytes": tot_bytes, "GBps": tot_bytes / tot_ms / 1e6,
                       "frac_of_peak": tot_bytes / tot_ms / 1e6 / PEAK_HBM_GBPS,
                       "rows_per_s": wl.rows / (tot_ms / 1e3)}
+    # The whole step: every operation of the workload (BatchNorm workloads
+    # with an eval step: training forward, backward and the eval forward).
+    st_bytes = sum(bench.bytes[op] for op in bench.ops)
+    st_ms = sum(res[op]["ms_mean"] for op in bench.ops)
+    res["step"] = {"ops": list(bench.ops), "ms": st_ms, "bytes": st_bytes,
+                   "GBps": st_bytes / st_ms / 1e6, "frac_of_peak": st_bytes / st_ms / 1e6 / PEAK_HBM_GBPS,
+                   "rows_per_s": wl.rows / (st_ms / 1e3)}
     names, main = meas["names"][bench.dominant]
     km = float(np.mean(meas["main"][bench.dominant]))
     kb = bench.bytes[bench.dominant + "_kernel"]
@@ -410,22 +474,38 @@ def load_traffic(kernel_key):
 
 
 def cpu_baseline(bench, budget_s):
+    """The float64 C oracle (as it stands; OpenMP over rows or channels) on
+    the host cores, timed on the same workload: groups of whole rows,
+    channels or element blocks, each group as large as one row / channel per
+    OpenMP thread (at least 1/16 of the workload), cycling through the
+    workload until `budget_s` seconds of oracle time have been spent (at
+    least one group).  Converting a group to float64 is outside the timing.
+    The rate is the workload's step bytes scaled by the fraction of it
+    processed, over the time spent."""
     import oracle
     wl = bench.wl
-    bf16 = wl.dtype == "bf16"
-    if wl.kind in ("ln", "rms"):
-        arrays = {k: oracle.widen(v, bf16=bf16) if v is not None else None
-                  for k, v in bench.inp.items()}
-    else:
-        raise NotImplementedError
-    reps, spent = 0, 0.0
-    while spent < budget_s and reps < 50:
+    units = bench.cpu_units()
+    threads = oracle.num_threads()
+    group = max(threads, -(-units // 16))
+    group = min(group, units)
+    done, spent, calls = 0, 0.0, 0
+    u0 = 0
+    while spent < budget_s or calls == 0:
+        u1 = min(u0 + group, units)
+        arrays = bench.cpu_prepare(oracle, u0, u1)
         t0 = time.perf_counter()
         bench.cpu_step(oracle, arrays)
         spent += time.perf_counter() - t0
-        reps += 1
-    per_step = spent / reps
-    tot_bytes = bench.bytes["fwd"] + bench.bytes["bwd"]
+        del arrays
+        done += u1 - u0
+        calls += 1
+        u0 = 0 if u1 >= units else u1
+        if calls >= 200:
+            break
+    frac = done / units
+    step_bytes = sum(bench.bytes[op] for op in bench.ops)
+    per_step = spent / frac
+    unit_name = {"bn": "channels", "ad": "blocks of 65536 elements"}.get(wl.kind, "rows")
     model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -434,10 +514,12 @@ def cpu_baseline(bench, budget_s):
                 break
     except OSError:
         pass
-    return {"value": tot_bytes / per_step / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+    return {"value": step_bytes / per_step / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"the whole {wl.name} workload (fwd+bwd, float64 C oracle, OpenMP over rows), "
-                      f"{reps} repetition(s), {spent:.1f} s total; inputs pre-widened to float64",
+            "sample": f"{wl.name}: {calls} oracle call(s) on groups of {group} of its {units} "
+                      f"{unit_name} ({done} {unit_name} = {frac:.3g} of the workload's step: "
+                      f"{', '.join(bench.ops)}), {spent:.1f} s; float64 C oracle, OpenMP; inputs "
+                      f"widened to float64 outside the timing",
             "s_per_step": per_step, "rows_per_s": wl.rows / per_step, "cpu_model": model}
 
 
@@ -466,8 +548,11 @@ def main():
     meas = measure(bench, args.steps, args.warmup, torch, hip, nl, flush)
     head = summarize(bench, meas)
     wall = meas["wall"]
-    print(f"[bench] {name}: fwd {head['fwd']['ms_mean']*1e3:.1f} us  bwd {head['bwd']['ms_mean']*1e3:.1f} us  "
-          f"fwd+bwd {head['fwd_bwd']['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+    print(f"[bench] {name}: " + "  ".join(f"{op} {head[op]['ms_mean']*1e3:.1f} us" for op in bench.ops)
+          + f"  step {head['step']['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+    cpu = cpu_baseline(bench, args.cpu_seconds) if not args.no_cpu else None
+    if hasattr(bench, "inp"):
+        del bench.inp
 
     per = {}
     if not args.no_others:
@@ -477,6 +562,8 @@ def main():
             ow = every[other]
             b = bench_class(ow)(ow, nl, torch)
             per[other] = summarize(b, measure(b, args.other_steps, 3, torch, hip, nl, flush))
+            if not args.no_cpu:
+                per[other]["cpu_baseline"] = cpu_baseline(b, args.other_cpu_seconds)
             print(f"[bench] {other}: " + "  ".join(
                 f"{op} {per[other][op]['ms_mean']*1e3:.1f} us {per[other][op]['GBps']:.0f} GB/s"
                 for op in b.ops), file=sys.stderr, flush=True)
@@ -502,25 +589,28 @@ def main():
     roofline = {"bound": "hbm", "achieved": dk["GBps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": dk["GBps"] / PEAK_HBM_GBPS, "traffic": traffic, "kernel": dk["kernel"],
                 "bytes_per_launch": dk["bytes"], "avg_us": dk["avg_us"]}
-    fb = head["fwd_bwd"]
+    st = head["step"]
+    op_name = {"rms": "RMSNorm", "ln": "LayerNorm", "bn": "BatchNorm", "ad": "activation+dropout"}[wl.kind]
+    config = {"workload": name, "ops": " + ".join(
+                  {"fwd": "training fwd" if wl.kind == "bn" else "fwd", "bwd": "bwd",
+                   "eval": "eval fwd"}[op] for op in bench.ops) + f" ({op_name})",
+              "shape": list(wl.shape), "io_dtype": wl.dtype, "eps": wl.eps}
+    if wl.kind == "bn":
+        config.update(act=wl.act, residual=wl.residual, momentum=wl.momentum)
     out = {
-        "metric": METRIC, "value": fb["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": fb["ms"], "higher_is_better": True,
+        "metric": METRIC, "value": st["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": st["ms"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": name, "op": {"rms": "RMSNorm", "ln": "LayerNorm", "bn": "BatchNorm",
-                                             "ad": "activation+dropout"}[wl.kind] + " fwd+bwd",
-                   "shape": list(wl.shape), "io_dtype": wl.dtype, "eps": wl.eps},
-        "pct_of_peak": 100.0 * fb["frac_of_peak"], "rows_per_s": fb["rows_per_s"],
-        "fwd": head["fwd"], "bwd": head["bwd"],
+        "config": config,
+        "pct_of_peak": 100.0 * st["frac_of_peak"], "rows_per_s": st["rows_per_s"],
+        "fwd_bwd": head["fwd_bwd"],
+        **{op: head[op] for op in bench.ops},
         "wall_s_timed_region_incl_flush": wall,
         "copy_GBps_host_events": copy_gbps,
         "roofline": roofline,
         "per_workload": per,
     }
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(bench, args.cpu_seconds)
-    else:
-        out["cpu_baseline"] = None
+    out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

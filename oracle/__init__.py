@@ -16,7 +16,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libnorm_oracle.so")
+# NORM_ORACLE_LIB points the module at another build of norm_oracle.c (the
+# mutation test loads copies with one planted mistake each).
+_LIB_PATH = os.environ.get("NORM_ORACLE_LIB") or os.path.join(_HERE, "libnorm_oracle.so")
 _lib = None
 
 ACT = {"none": 0, "relu": 1, "gelu": 2, "sigmoid": 3, "tanh": 4, "silu": 5, "mish": 6,
@@ -49,7 +51,7 @@ def _load():
         "orc_bn_fwd_eval": [_I64, _I64, _I64, ctypes.c_double, ctypes.c_int, ctypes.c_double,
                             _D, _D, _D, _D, _D, _D, _D],
         "orc_bn_bwd": [_I64, _I64, _I64, ctypes.c_double, ctypes.c_int, ctypes.c_double,
-                       _D, _D, _D, _D, _D, _D, _D, _D, _D],
+                       _D, _D, _D, _D, _D, _D, _D, _D, _D, _D],
         "orc_welford": [_I64, _D, _D],
         "orc_philox4x32_10": [_U32P, _U32P, _U32P],
         "orc_dropout_keep": [_I64, ctypes.c_double, ctypes.c_uint64, ctypes.c_uint64, _U8P],
@@ -186,16 +188,24 @@ def bn_fwd_eval(x, running_mean, running_var, res=None, w=None, b=None, eps=1e-5
     return y
 
 
-def bn_bwd(dy, x, res=None, w=None, b=None, eps=1e-5, act="none", bf16=False, act_param=0.0):
-    """Returns (dx, dres, dw, db); dres is None when there is no residual."""
+def bn_bwd(dy, x, res=None, w=None, b=None, eps=1e-5, act="none", bf16=False, act_param=0.0,
+           grad_at=None):
+    """Returns (dx, dres, dw, db); dres is None when there is no residual.
+
+    grad_at: optional float64 array of x's shape; where it is not NaN, the
+    activation's derivative of that element is taken at that point instead
+    of at z (selects a one-sided derivative at a kink)."""
     dy = _f(dy, bf16); x = _f(x, bf16); res = _f(res, bf16)
     w = _f(w, bf16); b = _f(b, bf16)
+    if grad_at is not None:
+        grad_at = widen(grad_at)
+        assert grad_at.shape == x.shape
     Nb, C, HW = x.shape
     dx = np.empty_like(x)
     dres = np.empty_like(x) if res is not None else None
     dw = np.empty(C); db = np.empty(C)
     _load().orc_bn_bwd(Nb, C, HW, eps, ACT[act], float(act_param), _p(dy), _p(x), _p(res), _p(w), _p(b),
-                       _p(dx), _p(dres), _p(dw), _p(db))
+                       _p(grad_at), _p(dx), _p(dres), _p(dw), _p(db))
     return dx, dres, dw, db
 
 

@@ -355,8 +355,8 @@ void orc_bn_fwd_eval(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
  *   dx   = (w * rstd / n) * (n * dz - db - xhat * dw).                    */
 void orc_bn_bwd(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
                 double act_p, const double *dy, const double *x, const double *res,
-                const double *w, const double *b, double *dx, double *dres,
-                double *dw, double *db) {
+                const double *w, const double *b, const double *grad_at, double *dx,
+                double *dres, double *dw, double *db) {
     double *mu = (double *)malloc(sizeof(double) * (C > 0 ? C : 1));
     double *var = (double *)malloc(sizeof(double) * (C > 0 ? C : 1));
     orc_bn_stats(Nb, C, HW, x, mu, var);
@@ -371,6 +371,7 @@ void orc_bn_bwd(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
                 int64_t idx = (bi * C + c) * HW + k;
                 double xhat = (x[idx] - mu[c]) * r;
                 double z = xhat * wc + bc + (res ? res[idx] : 0.0);
+                if (grad_at && !isnan(grad_at[idx])) z = grad_at[idx];
                 double dz = dy[idx] * orc_act_grad(act, act_p, z);
                 if (dres) dres[idx] = dz;
                 sum_dz += dz;
@@ -381,6 +382,7 @@ void orc_bn_bwd(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
                 int64_t idx = (bi * C + c) * HW + k;
                 double xhat = (x[idx] - mu[c]) * r;
                 double z = xhat * wc + bc + (res ? res[idx] : 0.0);
+                if (grad_at && !isnan(grad_at[idx])) z = grad_at[idx];
                 double dz = dy[idx] * orc_act_grad(act, act_p, z);
                 dx[idx] = (wc * r / n) * (n * dz - sum_dz - xhat * sum_dz_xhat);
             }

@@ -73,10 +73,16 @@ void orc_bn_fwd_eval(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
                      double act_p, const double *x, const double *res, const double *w,
                      const double *b, const double *running_mean,
                      const double *running_var, double *y);
+/* grad_at (nullable, [Nb][C][HW]): where it holds a number rather than NaN,
+ * the activation's derivative for that element is taken at that point
+ * instead of at z.  At a kink, where both one-sided derivatives are valid
+ * answers and a pre-activation within rounding of the kink may be rounded
+ * to either side, a caller passes a point just left or right of the kink to
+ * select one side. */
 void orc_bn_bwd(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
                 double act_p, const double *dy, const double *x, const double *res,
-                const double *w, const double *b, double *dx, double *dres,
-                double *dw, double *db);
+                const double *w, const double *b, const double *grad_at, double *dx,
+                double *dres, double *dw, double *db);
 
 /* The one-pass statistics the BatchNorm page describes, used only to show
  * that they reach the two-pass result: Welford's per-value update, and the

@@ -111,6 +111,44 @@ def to_io(a, dtype):
     return _to_io(a, dtype)
 
 
+# ------------------------------------------------------------- guard bands
+# Every output a GPU test checks sits inside a larger buffer whose GUARD
+# elements on each side hold a fixed NaN bit pattern; after the call the
+# bands must be bitwise unchanged, so a store past either end of an output
+# (the masked tails of [NormPage] "Engineering tricks") cannot go unseen.
+GUARD = 64
+_PATTERN = {4: (torch.int32, 0x7FC0DEAD), 2: (torch.int16, 0x7FDA), 1: (torch.uint8, 0xA5)}
+
+
+class Guarded:
+    """A device tensor of `shape` and `dtype` at element offset
+    GUARD + misalign of a buffer filled with the guard pattern.  misalign = 1
+    leaves the tensor off 16-byte alignment (the scalar paths).  `fill`
+    (a tensor) initializes it; otherwise it holds the pattern too."""
+
+    def __init__(self, shape, dtype, fill=None, misalign=0, device="cuda"):
+        shape = tuple(int(d) for d in shape)
+        self.n = int(np.prod(shape)) if shape else 1
+        es = torch.empty(0, dtype=dtype).element_size()
+        itype, self.pattern = _PATTERN[es]
+        self.off = GUARD + misalign
+        self.raw = torch.full((self.n + self.off + GUARD,), self.pattern, dtype=itype, device=device)
+        self.t = self.raw.view(dtype)[self.off:self.off + self.n].view(shape)
+        if fill is not None:
+            self.t.copy_(fill.reshape(shape))
+
+    def intact(self):
+        head, tail = self.raw[:self.off], self.raw[self.off + self.n:]
+        return bool((head == self.pattern).all()) and bool((tail == self.pattern).all())
+
+
+def assert_guards(named):
+    """named: {name: Guarded}; every guard band must be unchanged."""
+    torch.cuda.synchronize()
+    bad = [k for k, g in named.items() if g is not None and not g.intact()]
+    assert not bad, f"store outside the output: {bad}"
+
+
 # Pre-activation values where an activation's derivative jumps (PyTorch's
 # definitions; CELU and the smooth ones have none, softplus's switch to the
 # identity at 20 moves values by about 2e-9 only).
@@ -118,40 +156,102 @@ KINKS = {"relu": (0.0,), "leaky_relu": (0.0,), "elu": (0.0,), "selu": (0.0,),
          "relu6": (0.0, 6.0), "hardsigmoid": (-3.0, 3.0), "hardswish": (-3.0, 3.0)}
 
 
-def avoid_kinks(orc, inp, dtype, eps, act, delta=1e-3, step=None):
-    """Move the residual (or x) so no pre-activation lies within `delta` of a
-    kink of `act`.
+# Rounding radius of the kernels' float32 pre-activation.  The kernels form
+# z = x * a + s (+ res) with a = w * rstd and s = b - mean * a, from float32
+# statistics; every term carries a few float32 roundings, so the computed z
+# lies within a few ulps of the largest term of the exact z.  KINK_ULPS
+# float32 ulps of T = |x a| + |mean a| + |b| + |res| bounds that (the
+# statistics' own float32 errors included) with room to spare, and is still
+# about 2e-6 * T wide.
+KINK_ULPS = 32
+
+
+def kink_radius(orc, inp, dtype, eps):
+    """Per-element radius within which the kernels' float32 z may fall on
+    either side of a kink (oracle statistics; float64)."""
+    bf16 = dtype == "bf16"
+    _, mean, rstd, _, _ = orc.bn_fwd_train(inp["x"], None, inp["w"], inp["b"], eps=eps,
+                                           act="none", bf16=bf16)
+    C = mean.shape[0]
+    w = orc.widen(inp["w"], bf16=bf16) if inp["w"] is not None else np.ones(C)
+    b = orc.widen(inp["b"], bf16=bf16) if inp["b"] is not None else np.zeros(C)
+    a = (w * rstd)[None, :, None]
+    T = np.abs(orc.widen(inp["x"], bf16=bf16) * a) + np.abs(mean[None, :, None] * a) + \
+        np.abs(b)[None, :, None]
+    if inp.get("res") is not None:
+        T = T + np.abs(orc.widen(inp["res"], bf16=bf16))
+    return KINK_ULPS * 2.0 ** -24 * T
+
+
+def oracle_z(orc, inp, dtype, eps):
+    """The exact pre-activation z (float64) of the BatchNorm forward."""
+    z, _, _, _, _ = orc.bn_fwd_train(inp["x"], inp.get("res"), inp["w"], inp["b"], eps=eps,
+                                     act="none", bf16=dtype == "bf16")
+    return z
+
+
+def relu_kink_sides(orc, inp, dtype, eps, y_gpu):
+    """ReLU on unedited inputs: at every element whose exact z lies within
+    the rounding radius of 0 both one-sided derivatives are valid, and the
+    kernels' float32 z may have been rounded to either side.  The side the
+    GPU took is read from its own forward output (y > 0 exactly when its z
+    was > 0; the backward recomputes the same z bit for bit, so a backward
+    that disagrees with its forward fails the comparison).  Returns the
+    oracle's grad_at array (NaN except at those elements, where it holds a
+    point just right or left of 0) and their number."""
+    z = oracle_z(orc, inp, dtype, eps)
+    amb = np.abs(z) < kink_radius(orc, inp, dtype, eps)
+    grad_at = np.full(z.shape, np.nan)
+    if amb.any():
+        side = to_f64(y_gpu).reshape(z.shape)[amb] > 0
+        grad_at[amb] = np.where(side, 2.0 ** -60, -(2.0 ** -60))
+    return grad_at, int(amb.sum())
+
+
+def avoid_kinks(orc, inp, dtype, eps, act, step=None):
+    """Move the residual (or x) so that no pre-activation lies within the
+    kernels' rounding radius (kink_radius) of a kink of `act`.
 
     Where the derivative jumps, an element whose z is within rounding
     distance of the kink has two valid gradients (the GPU's float32 z and the
     oracle's float64 z may fall on different sides).  The test inputs are
-    shifted away from every kink, using the oracle's z, so the choice is
-    unique.  Returns the edited copy of `inp` and the number of elements
-    moved."""
+    shifted away from every such kink, using the oracle's z, so the choice is
+    unique.  The radius is a few dozen float32 ulps of the terms z is formed
+    from, so on the small test shapes almost no element moves.  Returns the
+    edited copy of `inp` and the number of elements moved."""
     kinks = np.asarray(KINKS.get(act, ()), dtype=np.float64)
     out = dict(inp)
     if kinks.size == 0:
         return out, 0
     bf16 = dtype == "bf16"
-    step = step if step is not None else {"bf16": 0.0625, "f16": 1.0 / 64}.get(dtype, 4 * delta)
     moved = 0
     for _ in range(6):
-        y, _, _, _, _ = orc.bn_fwd_train(out["x"], out["res"], out["w"], out["b"], eps=eps,
-                                         act="none", bf16=bf16)
-        d = y[..., None] - kinks
+        z = oracle_z(orc, out, dtype, eps)
+        delta = kink_radius(orc, out, dtype, eps)
+        d = z[..., None] - kinks
         j = np.abs(d).argmin(axis=-1)
         nearest = np.take_along_axis(d, j[..., None], axis=-1)[..., 0]
         near = np.abs(nearest) < delta
         if not near.any():
             return out, moved
         moved += int(near.sum())
-        shift = np.where(nearest >= 0, step, -step)
-        key = "res" if out["res"] is not None else "x"
+        key = "res" if out.get("res") is not None else "x"
         base = orc.widen(out[key], bf16=bf16)
+        # A step of 4 radii (or, for 16-bit inputs, one step of the format
+        # near the value) clears the band; float32 rounding of the edit is
+        # far below it.
+        if step is not None:
+            st = step
+        elif dtype == "f32":
+            st = 4.0 * delta
+        else:
+            ulp = ulp_bf16 if bf16 else ulp_f16
+            st = np.maximum(4.0 * delta, 2.0 * ulp(np.maximum(np.abs(base), 1e-30)))
+        shift = np.where(nearest >= 0, st, -st)
         edited = (base + np.where(near, shift, 0.0)).astype(np.float32)
         out[key] = to_io(edited, dtype)
     raise AssertionError(f"could not move the pre-activations away from the {act} kinks")
 
 
-def avoid_relu_kink(orc, inp, dtype, eps, delta=1e-3, step=None):
-    return avoid_kinks(orc, inp, dtype, eps, "relu", delta, step)
+def avoid_relu_kink(orc, inp, dtype, eps, step=None):
+    return avoid_kinks(orc, inp, dtype, eps, "relu", step)

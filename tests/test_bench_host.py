@@ -74,3 +74,48 @@ def test_multi_gpu_request_exits_with_message():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def _host_bench(cls, wl, inp, **attrs):
+    """A bench object with host inputs only (no device tensors): enough for
+    the CPU-baseline leg."""
+    b = object.__new__(cls)
+    b.wl, b.inp = wl, inp
+    for k, v in attrs.items():
+        setattr(b, k, v)
+    return b
+
+
+@pytest.mark.parametrize("name", ["bn_bf16_256x64x112x112", "bn_f32_64x256x56x56", "rms_bf16_16384x4096",
+                                  "actdrop_bf16_16384x4096"])
+def test_cpu_baseline_on_a_small_variant(name):
+    """The oracle timing leg on a shrunken copy of each workload kind: it
+    cycles over groups of channels / rows / element blocks, reports the
+    threads used and what was sampled."""
+    import dataclasses
+
+    import numpy as np
+
+    from normalization_ln_rmsnorm_amd import workloads as W
+    wl = {**WORKLOADS, **EXTRA_WORKLOADS}[name]
+    if wl.kind == "bn":
+        wl = dataclasses.replace(wl, shape=(4, 8, 7, 7))
+        b = _host_bench(bench.BnBench, wl, W.gen_bn(wl), ops=["fwd", "bwd"] + (
+            ["eval"] if wl.eval_after_train else []), bytes=bench.bytes_bn(wl, bench.ELEM_SIZE[wl.dtype]))
+    elif wl.kind == "ad":
+        wl = dataclasses.replace(wl, shape=(3, 70000))
+        inp = W.gen_act_dropout(wl)
+
+        class _X:  # numel() of the device input
+            def numel(self):
+                return inp["x"].size
+        b = _host_bench(bench.AdBench, wl, inp, ops=["fwd", "bwd"], x=_X(), p=0.1, seed=7,
+                        bytes=bench.bytes_act_dropout(wl, 2))
+    else:
+        wl = dataclasses.replace(wl, shape=(40, 256))
+        b = _host_bench(bench.RowBench, wl, W.gen_rowwise(wl), ops=["fwd", "bwd"],
+                        bytes=bench.bytes_rowwise(wl.kind, 40, 256, bench.ELEM_SIZE[wl.dtype]))
+    r = bench.cpu_baseline(b, 0.05)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0
+    assert r["cores"] >= 1 and np.isfinite(r["s_per_step"])
+    assert name in r["sample"]

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests._parity import check, to_dev, to_f64, to_io
+from tests._parity import TORCH_DTYPE, Guarded, assert_guards, check, to_dev, to_f64, to_io
 
 pytestmark = pytest.mark.gpu
 
@@ -23,16 +23,20 @@ def _inputs(dtype, n, seed):
     return gen_act_dropout(dataclasses.replace(WL, dtype=dtype), n=n, seed=seed)
 
 
-def run_case(orc, dtype, n, act, p, seed, offset, param=0.0, x_dev=None):
+def run_case(orc, dtype, n, act, p, seed, offset, param=0.0, x_dev=None, misalign=0):
+    """Outputs sit between guard bands; misalign=1 places them off 16-byte
+    alignment."""
     inp = _inputs(dtype, n, seed=(seed ^ n) & 0xFFFF)
     bf16 = dtype == "bf16"
     x = to_dev(inp["x"], dtype) if x_dev is None else x_dev(inp["x"])
     dy = to_dev(inp["dy"], dtype)
     p32 = float(np.float32(p))  # the kernels see p as float32
-    y = nl.act_dropout_fwd(x, act, p, seed, offset, act_param=param)
-    ynone = nl.act_dropout_fwd(x, "none", p, seed, offset)
-    dx = nl.act_dropout_bwd(dy, x, act, p, seed, offset, act_param=param)
-    torch.cuda.synchronize()
+    tdt = TORCH_DTYPE[dtype]
+    G = {k: Guarded((n,), tdt, misalign=misalign) for k in ("y", "ynone", "dx")}
+    y = nl.act_dropout_fwd(x, act, p, seed, offset, act_param=param, y=G["y"].t)
+    ynone = nl.act_dropout_fwd(x, "none", p, seed, offset, y=G["ynone"].t)
+    dx = nl.act_dropout_bwd(dy, x, act, p, seed, offset, act_param=param, dx=G["dx"].t)
+    assert_guards(G)
     keep = orc.dropout_keep(n, p32, seed, offset)
     # x has no exact zeros, so the identity activation exposes the mask.
     assert (orc.widen(inp["x"], bf16=bf16) != 0).all()
@@ -97,7 +101,16 @@ def test_unaligned_tensors_take_the_scalar_path(orc, dtype):
         big = torch.empty(t.numel() + 1, dtype=tdt, device="cuda")
         big[1:].copy_(t)
         return big[1:]
-    run_case(orc, dtype, 3001, "gelu", 0.25, seed=5, offset=8, x_dev=shifted)
+    run_case(orc, dtype, 3001, "gelu", 0.25, seed=5, offset=8, x_dev=shifted, misalign=1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("n", [1, 5, 4097, 100003])
+def test_unaligned_outputs(orc, dtype, n):
+    """Aligned input, outputs one element off 16-byte alignment (the scalar
+    path), with guard bands."""
+    print(f"case act_dropout unaligned outputs {dtype} n={n}", flush=True)
+    run_case(orc, dtype, n, "silu", 0.2, seed=11, offset=4, misalign=1)
 
 
 def test_full_size_workload(orc):
@@ -106,9 +119,10 @@ def test_full_size_workload(orc):
     inp = gen_act_dropout(WL)
     x, dy = to_dev(inp["x"], "bf16"), to_dev(inp["dy"], "bf16")
     p, seed = WL.extra["drop_p"], WL.extra["dropout_seed"]
-    y = nl.act_dropout_fwd(x, WL.act, p, seed, 0)
-    dx = nl.act_dropout_bwd(dy, x, WL.act, p, seed, 0)
-    torch.cuda.synchronize()
+    G = {k: Guarded((M * N,), torch.bfloat16) for k in ("y", "dx")}
+    y = nl.act_dropout_fwd(x, WL.act, p, seed, 0, y=G["y"].t)
+    dx = nl.act_dropout_bwd(dy, x, WL.act, p, seed, 0, dx=G["dx"].t)
+    assert_guards(G)
     p32 = float(np.float32(p))
     ry = orc.act_dropout_fwd(inp["x"], WL.act, p32, seed, 0, bf16=True)
     check("full y", to_f64(y), ry, "bf16")

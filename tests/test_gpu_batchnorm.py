@@ -2,8 +2,17 @@
 the fused residual and each fused activation) through the C ABI against the
 float64 oracle, element by element.
 
-Cases whose activation has a derivative jump move the inputs off the kinks
-first (tests._parity.avoid_kinks): at a kink either gradient is valid.
+Every output (y, y_eval, dx, dres, dw, db, the saved and running statistics
+and the workspace) sits between guard bands that must come back unchanged.
+
+At a kink of the activation, an element whose exact pre-activation lies
+within the kernels' float32 rounding radius of the kink has two valid
+gradients.  Small cases move such elements off the kink first
+(tests._parity.avoid_kinks; the radius is a few dozen float32 ulps of the
+terms z is formed from, so almost none move).  The full-size ReLU workload
+runs on the benchmark's unedited inputs: there the side the GPU took at each
+such element is read from its forward output and handed to the oracle
+(tests._parity.relu_kink_sides).
 """
 import dataclasses
 
@@ -11,12 +20,25 @@ import numpy as np
 import pytest
 import torch
 
-from tests._parity import avoid_kinks, check, to_dev, to_f64, to_io
+from tests._parity import (TORCH_DTYPE, Guarded, assert_guards, avoid_kinks, check,
+                           relu_kink_sides, to_dev, to_f64, to_io)
 
 pytestmark = pytest.mark.gpu
 
 nl = pytest.importorskip("normalization_ln_rmsnorm_amd")
 from normalization_ln_rmsnorm_amd.workloads import EXTRA_WORKLOADS, WORKLOADS, gen_bn  # noqa: E402
+
+
+@pytest.fixture
+def force_path():
+    """Pins BatchNorm's data path for one test (restored afterwards)."""
+    prev = []
+
+    def set_path(path):
+        prev.append(nl.bn_force_path(path))
+    yield set_path
+    if prev:
+        nl.bn_force_path(prev[0])
 
 
 def _wl(dtype, act, residual):
@@ -33,7 +55,10 @@ def _scale_w(orc, inp, dtype, k):
 
 
 def run_case(orc, dtype, Nb, C, HW, act, residual, with_wb=True, eval_after=True, report=None,
-             inp=None, wl=None, act_param=0.0, w_scale=1):
+             inp=None, wl=None, act_param=0.0, w_scale=1, raw=False, misalign=0):
+    """raw=True keeps the inputs unedited (ReLU: the GPU's side at elements
+    within rounding of the kink goes to the oracle); misalign=1 places every
+    streamed output off 16-byte alignment (the scalar paths)."""
     wl = wl or _wl(dtype, act, residual)
     if inp is None:
         inp = gen_bn(wl, Nb=Nb, C=C, HW=HW)
@@ -41,32 +66,57 @@ def run_case(orc, dtype, Nb, C, HW, act, residual, with_wb=True, eval_after=True
     eps, mom = wl.eps, wl.momentum
     if w_scale != 1:
         inp = _scale_w(orc, inp, dtype, w_scale)
-    inp, moved = avoid_kinks(orc, inp, dtype, eps, act)
+    inp = dict(inp)
+    if not residual:
+        inp["res"] = None
+    if not with_wb:
+        inp["w"] = inp["b"] = None
+    if raw:
+        assert act in ("relu", "none") and dtype in ("f32", "bf16"), "raw inputs: ReLU, f32/bf16"
+        moved = 0
+    else:
+        inp, moved = avoid_kinks(orc, inp, dtype, eps, act)
+    tdt = TORCH_DTYPE[dtype]
     shape = (Nb, C, HW)
     x = to_dev(inp["x"], dtype)
     res = to_dev(inp["res"], dtype) if residual else None
     w = to_dev(inp["w"], dtype) if with_wb else None
     b = to_dev(inp["b"], dtype) if with_wb else None
     dy = to_dev(inp["dy"], dtype)
-    rm = torch.from_numpy(inp["running_mean"].copy()).cuda()
-    rv = torch.from_numpy(inp["running_var"].copy()).cuda()
-    w_np = inp["w"] if with_wb else None
-    b_np = inp["b"] if with_wb else None
-    res_np = inp["res"] if residual else None
+    w_np, b_np, res_np = inp["w"], inp["b"], inp["res"]
+
+    G = dict(y=Guarded(shape, tdt, misalign=misalign), dx=Guarded(shape, tdt, misalign=misalign),
+             sm=Guarded((C,), torch.float32), sr=Guarded((C,), torch.float32),
+             rm=Guarded((C,), torch.float32, fill=torch.from_numpy(inp["running_mean"].copy())),
+             rv=Guarded((C,), torch.float32, fill=torch.from_numpy(inp["running_var"].copy())),
+             dres=Guarded(shape, tdt, misalign=misalign) if residual else None,
+             dw=Guarded((C,), tdt) if with_wb else None, db=Guarded((C,), tdt) if with_wb else None,
+             ye=Guarded(shape, tdt, misalign=misalign) if eval_after else None,
+             ws=Guarded((max(1, nl.bn_workspace_bytes(tdt, Nb, C, HW)),), torch.uint8))
+    t = {k: (g.t if g is not None else None) for k, g in G.items()}
+    rm, rv = t["rm"], t["rv"]
 
     ap = act_param
-    y, sm, sr = nl.bn_fwd_train(x, w, b, rm, rv, eps, mom, act, res, act_param=ap)
+    y, sm, sr = nl.bn_fwd_train(x, w, b, rm, rv, eps, mom, act, res, act_param=ap, y=t["y"],
+                                save_mean=t["sm"], save_rstd=t["sr"], ws=t["ws"])
     dx, dres, dw, db = nl.bn_bwd(dy, x, w, b, sm, sr, act, res, act_param=ap, want_dw=with_wb,
-                                 want_db=with_wb)
-    ye = nl.bn_fwd_eval(x, w, b, rm, rv, eps, act, res, act_param=ap) if eval_after else None
-    torch.cuda.synchronize()
+                                 want_db=with_wb, dx=t["dx"], dres=t["dres"], dw=t["dw"],
+                                 db=t["db"], ws=t["ws"])
+    ye = nl.bn_fwd_eval(x, w, b, rm, rv, eps, act, res, act_param=ap, y=t["ye"]) if eval_after else None
+    assert_guards(G)
 
+    grad_at, n_amb = None, 0
+    if raw and act == "relu":
+        grad_at, n_amb = relu_kink_sides(orc, inp, dtype, eps, y)
     ry, rsm, rsr, rrm, rrv = orc.bn_fwd_train(inp["x"], res_np, w_np, b_np, inp["running_mean"],
                                               inp["running_var"], eps=eps, momentum=mom, act=act,
                                               bf16=bf16, act_param=ap)
     rdx, rdres, rdw, rdb = orc.bn_bwd(inp["dy"], inp["x"], res_np, w_np, b_np, eps=eps, act=act,
-                                      bf16=bf16, act_param=ap)
+                                      bf16=bf16, act_param=ap, grad_at=grad_at)
     tag = f"bn/{dtype}/{Nb}x{C}x{HW}/{act}({ap})/res={residual}"
+    if moved or n_amb:
+        print(f"{tag}: {moved} elements moved off a kink, {n_amb} within rounding of one "
+              "(the GPU's side taken)", flush=True)
     ch = (0, 2)  # bf16 floor taken per channel
     check(f"{tag} y", to_f64(y), ry, dtype, group_axis=ch, report=report)
     check(f"{tag} save_mean", to_f64(sm), rsm, "f32", report=report)
@@ -77,8 +127,12 @@ def run_case(orc, dtype, Nb, C, HW, act, residual, with_wb=True, eval_after=True
     # channel, dz = dy * act'(z) (oracle values).
     wabs = np.abs(orc.widen(w_np, bf16=bf16)) if with_wb else np.ones(C)
     z, _, _, _, _ = orc.bn_fwd_train(inp["x"], res_np, w_np, b_np, eps=eps, act="none", bf16=bf16)
+    if grad_at is not None:
+        z = np.where(np.isnan(grad_at), z, grad_at)
     dz = orc.widen(inp["dy"], bf16=bf16) * orc.act(act, z, grad=True, param=ap)
+    del z
     dx_scale = (wabs * rsr * np.abs(dz).max(axis=(0, 2)))[None, :, None]
+    del dz
     check(f"{tag} dx", to_f64(dx), rdx, dtype, group_axis=ch, report=report, scale=dx_scale)
     if residual:
         check(f"{tag} dres", to_f64(dres), rdres, dtype, group_axis=ch, report=report)
@@ -91,6 +145,7 @@ def run_case(orc, dtype, Nb, C, HW, act, residual, with_wb=True, eval_after=True
         rye = orc.bn_fwd_eval(inp["x"], to_f64(rm), to_f64(rv), res_np, w_np, b_np, eps=eps,
                               act=act, bf16=bf16, act_param=ap)
         check(f"{tag} y_eval", to_f64(ye), rye, dtype, group_axis=ch, report=report)
+    return n_amb
 
 
 SMALL = [(2, 3, 5), (4, 8, 49), (3, 5, 1), (2, 4, 7), (5, 16, 64), (2, 2, 3136), (7, 3, 1000),
@@ -141,14 +196,38 @@ def test_two_values_pin_unbiased_running_var(orc):
 
 @pytest.mark.parametrize("name", ["bn_f32_64x256x56x56", "bn_bf16_256x64x112x112"])
 def test_full_size_workloads(orc, name):
+    """The two BatchNorm2d workloads at full size on the benchmark's own
+    (unedited) inputs and launch configuration; for ReLU the GPU's side at
+    the elements within rounding of the kink is handed to the oracle."""
     wl = WORKLOADS[name]
     Nb, C, H, W = wl.shape
     print(f"case {name}", flush=True)
     report = []
-    run_case(orc, wl.dtype, Nb, C, H * W, wl.act, wl.residual, eval_after=True, report=report,
-             wl=wl)
+    n_amb = run_case(orc, wl.dtype, Nb, C, H * W, wl.act, wl.residual, eval_after=True,
+                     report=report, wl=wl, raw=wl.act in ("relu", "none"))
     for r in report:
         print(r, flush=True)
+    print(f"{name}: {n_amb} elements within rounding of the ReLU kink", flush=True)
+
+
+@pytest.mark.parametrize("path", ["plane", "cols"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("Nb,C,HW", [(4, 8, 49), (7, 3, 1000), (3, 5, 1), (33, 7, 13)])
+def test_unaligned_outputs_scalar_tails(orc, force_path, path, dtype, Nb, C, HW):
+    """Every streamed output one element off 16-byte alignment (the scalar
+    path of each kernel), on both data paths, with guard bands."""
+    force_path(path)
+    print(f"case bn unaligned path={path} {dtype} {Nb}x{C}x{HW}", flush=True)
+    run_case(orc, dtype, Nb, C, HW, "gelu", True, misalign=1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Nb,C,HW", [(8, 16, 3136), (64, 64, 1)])
+def test_relu_raw_inputs(orc, dtype, Nb, C, HW):
+    """ReLU + residual on unedited inputs (the full-size workload's method at
+    a size with many elements near the kink relative to the radius)."""
+    print(f"case bn relu raw {dtype} {Nb}x{C}x{HW}", flush=True)
+    run_case(orc, dtype, Nb, C, HW, "relu", True, raw=True)
 
 
 # BatchNorm1d shapes: (N, C) with HW = 1 and (N, C, L); they take the
@@ -169,10 +248,10 @@ def test_bn1d_shapes(orc, dtype, act, residual, Nb, C, HW):
 @pytest.mark.parametrize("path", ["plane", "cols"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("Nb,C,HW", [(4, 8, 49), (7, 3, 1000), (8, 16, 64), (300, 40, 1)])
-def test_each_path_on_every_shape(orc, monkeypatch, path, dtype, Nb, C, HW):
+def test_each_path_on_every_shape(orc, force_path, path, dtype, Nb, C, HW):
     """Either data path, forced, meets the tolerance on shapes that would
     normally take the other."""
-    monkeypatch.setenv("MI355NORM_BN_PATH", path)
+    force_path(path)
     print(f"case bn path={path} {dtype} {Nb}x{C}x{HW}", flush=True)
     run_case(orc, dtype, Nb, C, HW, "gelu", True)
 
@@ -349,7 +428,7 @@ def test_long_planes(orc, dtype):
 
 @pytest.mark.parametrize("path", ["plane", "cols"])
 @pytest.mark.parametrize("act,residual", [("relu", True), ("gelu", False)])
-def test_f32_channels_far_from_zero(orc, monkeypatch, path, act, residual):
+def test_f32_channels_far_from_zero(orc, force_path, path, act, residual):
     """float32 channels whose mean is up to ~50 spreads from zero: the
     recipe's channels moved by a per-channel offset of 10-25 (either sign).
     The statistics fold values relative to a per-tile shift and the
@@ -358,7 +437,7 @@ def test_f32_channels_far_from_zero(orc, monkeypatch, path, act, residual):
     range: its rounding moves every z of the channel alike, and with GELU
     db (a sum of n derivatives) reaches the tolerance near |mean| / std ~
     100."""
-    monkeypatch.setenv("MI355NORM_BN_PATH", path)
+    force_path(path)
     Nb, C, HW = (4, 8, 3136) if path == "plane" else (256, 64, 1)
     inp = gen_bn(_wl("f32", act, residual), Nb=Nb, C=C, HW=HW)
     rng = np.random.default_rng(777)

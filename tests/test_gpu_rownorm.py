@@ -11,27 +11,12 @@ import numpy as np
 import pytest
 import torch
 
-from tests._parity import TORCH_DTYPE, check, to_dev, to_f64
+from tests._parity import TORCH_DTYPE, Guarded, assert_guards, check, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
 nl = pytest.importorskip("normalization_ln_rmsnorm_amd")
 from normalization_ln_rmsnorm_amd.workloads import WORKLOADS, gen_rowwise  # noqa: E402
-
-SENTINEL = float("nan")
-PAD = 64
-
-
-def _guarded(shape, dtype):
-    n = int(np.prod(shape))
-    buf = torch.full((n + 2 * PAD,), SENTINEL, dtype=dtype, device="cuda")
-    return buf, buf[PAD:PAD + n].view(*shape)
-
-
-def _guard_ok(buf, n):
-    head, tail = buf[:PAD], buf[PAD + n:]
-    return bool(torch.isnan(head.float()).all() and torch.isnan(tail.float()).all())
-
 
 def _wl(kind, dtype):
     """The workload whose value recipe a small case borrows."""
@@ -57,23 +42,34 @@ def run_case(orc, kind, dtype, M, N, with_w=True, with_b=True, eps=None, seed=No
     w_np = inp["w"] if with_w else None
     b_np = inp["b"] if (with_b and kind == "ln") else None
 
-    ybuf, y = _guarded((M, N), tdt) if guard else (None, torch.empty(M, N, dtype=tdt, device="cuda"))
-    dxbuf, dx = _guarded((M, N), tdt) if guard else (None, torch.empty(M, N, dtype=tdt, device="cuda"))
-    if kind == "ln":
-        _, mean, rstd = nl.ln_fwd(x, w, b, eps, y=y)
-        dx_, dw, db = nl.ln_bwd(dy, x, w, mean, rstd, dx=dx, want_dw=with_w, want_db=with_b)
+    # Every output between guard bands (y, dx, the statistics, dw / db and
+    # the workspace).
+    ln = kind == "ln"
+    if guard:
+        wsn = (nl.ln_bwd_workspace_bytes if ln else nl.rms_bwd_workspace_bytes)(tdt, M, N)
+        G = dict(y=Guarded((M, N), tdt), dx=Guarded((M, N), tdt), rstd=Guarded((M,), torch.float32),
+                 mean=Guarded((M,), torch.float32) if ln else None,
+                 dw=Guarded((N,), tdt) if with_w else None,
+                 db=Guarded((N,), tdt) if (ln and with_b) else None,
+                 ws=Guarded((max(1, wsn),), torch.uint8))
+        t = {k: (g.t if g is not None else None) for k, g in G.items()}
+    else:
+        G, t = {}, dict(y=None, dx=None, rstd=None, mean=None, dw=None, db=None, ws=None)
+    if ln:
+        y, mean, rstd = nl.ln_fwd(x, w, b, eps, y=t["y"], mean=t["mean"], rstd=t["rstd"])
+        dx, dw, db = nl.ln_bwd(dy, x, w, mean, rstd, dx=t["dx"], want_dw=with_w, want_db=with_b,
+                               dw=t["dw"], db=t["db"], ws=t["ws"])
         ry, rmean, rrstd = orc.ln_fwd(inp["x"], w_np, b_np, eps=eps, bf16=bf16)
         rdx, rdw, rdb = orc.ln_bwd(inp["dy"], inp["x"], w_np, eps=eps, bf16=bf16)
     else:
-        _, rstd = nl.rms_fwd(x, w, eps, y=y)
-        dx_, dw = nl.rms_bwd(dy, x, w, rstd, dx=dx, want_dw=with_w)
+        y, rstd = nl.rms_fwd(x, w, eps, y=t["y"], rstd=t["rstd"])
+        dx, dw = nl.rms_bwd(dy, x, w, rstd, dx=t["dx"], want_dw=with_w, dw=t["dw"], ws=t["ws"])
         db = None
         ry, rrstd = orc.rms_fwd(inp["x"], w_np, eps=eps, bf16=bf16)
         rdx, rdw = orc.rms_bwd(inp["dy"], inp["x"], w_np, eps=eps, bf16=bf16)
     torch.cuda.synchronize()
     if guard:
-        assert _guard_ok(ybuf, M * N), "y: write outside the output"
-        assert _guard_ok(dxbuf, M * N), "dx: write outside the output"
+        assert_guards(G)
     tag = f"{kind}/{dtype}/{M}x{N}"
     check(f"{tag} y", to_f64(y), ry, dtype, group_axis=1, report=report)
     check(f"{tag} rstd", to_f64(rstd), rrstd, "f32", report=report)

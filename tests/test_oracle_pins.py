@@ -380,3 +380,38 @@ def test_bn_running_stats_unbiased_factor(orc):
         assert rm[0] == pytest.approx(m * 2.5, abs=1e-15)
         assert rv[0] == pytest.approx((1 - m) * 1.0 + m * 4.5, rel=1e-15)
         assert sr[0] == pytest.approx(1 / 1.5, rel=1e-15)
+
+
+# ------------------------------------------------ one-sided derivatives
+def test_grad_at_selects_the_one_sided_limit(orc):
+    """grad_at picks the derivative's side at a kink.  A channel [-1, 0, 1]
+    (w = 1, b = 0, no shift) puts z of its middle element exactly on the
+    ReLU kink.  The result with the right side selected must be the limit
+    of the plain backward as that element's residual moves up from 0 (z just
+    right of the kink), and the left side the limit from below; NaN entries
+    leave the plain backward unchanged bit for bit."""
+    x = np.array([[[-1.0, 0.0, 1.0], [-2.0, 0.0, 2.0]]])
+    dy = np.array([[[0.3, -0.7, 0.5], [1.1, 0.9, -0.4]]])
+    w, b = np.ones(2), np.zeros(2)
+    r = np.zeros_like(x)
+    eps = 1e-5
+    plain = orc.bn_bwd(dy, x, r, w, b, eps=eps, act="relu")
+    nan = np.full(x.shape, np.nan)
+    same = orc.bn_bwd(dy, x, r, w, b, eps=eps, act="relu", grad_at=nan)
+    for a, c in zip(plain, same):
+        assert np.array_equal(a, c)
+    for side in (1.0, -1.0):
+        at = nan.copy()
+        at[0, :, 1] = side * 2.0 ** -60
+        got = orc.bn_bwd(dy, x, r, w, b, eps=eps, act="relu", grad_at=at)
+        r2 = r.copy()
+        r2[0, :, 1] = side * 1e-9
+        lim = orc.bn_bwd(dy, x, r2, w, b, eps=eps, act="relu")
+        for a, c in zip(got, lim):
+            np.testing.assert_allclose(a, c, atol=1e-12)
+    # The right side passes the gradient through the kink element.
+    at = nan.copy()
+    at[0, :, 1] = 2.0 ** -60
+    _, dres, _, db = orc.bn_bwd(dy, x, r, w, b, eps=eps, act="relu", grad_at=at)
+    assert np.array_equal(dres[0, :, 1], dy[0, :, 1])
+    assert plain[1][0, 0, 1] == 0.0
