@@ -154,6 +154,27 @@ norm_status rms_bwd(norm_dtype dt, int64_t M, int64_t N, const void *dy,
                     void *dx, void *dw, void *ws, size_t ws_bytes,
                     void *stream);
 
+/* No-allocation variant of rms_bwd, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, results and
+ * kernels as rms_bwd without (ws, ws_bytes): the dw partial rows live in a
+ * static device array of NORM_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on until the process ends.  The call allocates and
+ * frees nothing.  It needs (partial rows of the launch plan) * N * 4 bytes
+ * of that array -- at most 512 partial rows on a 256-CU part, so N up to
+ * 8192 always fits, and M * N * 4 bytes whenever M is smaller than that --
+ * and returns NORM_ERR_WORKSPACE, before anything is launched, for a shape
+ * that needs more.  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (different streams, or host threads) race and
+ * must be serialized by the caller.  Nothing in the array needs to start at
+ * zero (every partial row is written before it is read); it keeps the last
+ * call's contents.  NORM_ERR_HIP if the runtime cannot resolve the array's
+ * address on the current device.                                          */
+#define NORM_NOALLOC_SCRATCH_BYTES (16u << 20)
+norm_status rms_bwd_noalloc(norm_dtype dt, int64_t M, int64_t N, const void *dy,
+                            const void *x, const void *w, const float *rstd,
+                            void *dx, void *dw, void *stream);
+
 /* ------------------------------------------------------------- BatchNorm
  * Workspace bytes for bn_fwd_train and bn_bwd at this shape (the same
  * buffer serves both; its contents on entry are ignored).               */

@@ -11,13 +11,16 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "row_common.hpp"
 
 namespace mi355norm {
 
 constexpr int64_t kDirectRowGroups = 8;  // backward: one block (no column-sum kernel) up to this
+constexpr size_t kScratchBytes = NORM_NOALLOC_SCRATCH_BYTES;  // static scratch of rms_bwd_noalloc
 
 // ---------------------------------------------------------------- planning
 
@@ -164,15 +167,55 @@ static norm_status fwd_entry(norm_dtype dt, int64_t M, int64_t N, float eps, con
     });
 }
 
+// ------------------------------------------------- static scratch (device)
+// The no-allocation backward keeps its partial rows in this file-scope
+// device array instead of a caller workspace.  Each GPU the library runs on
+// holds its own copy (zero at load) until the process ends.  Host code must
+// never pass the array's name to a kernel: on the host it is only a
+// stand-in for the symbol.  The device address is taken once per device
+// with hipGetSymbolAddress and used everywhere instead.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kScratchDevices];
+std::mutex g_scratch_mutex;
+}  // namespace
+
+// The current device's address of `scratch` (nullptr if the runtime fails).
+static void *static_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void *addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+        g_scratch_ptr[dev].store(addr, std::memory_order_release);
+        p = addr;
+    }
+    return p;
+}
+
 static size_t bwd_ws_bytes(norm_dtype dt, int64_t M, int64_t N, int nparts) {
     if (check_rows(dt, M, N) != NORM_OK) return 0;
     return (size_t)max_partial_rows(M) * (size_t)N * sizeof(float) * (size_t)nparts;
 }
 
+// Where the backward's partial rows go: the caller's workspace (sized by
+// the *_bwd_workspace_bytes query), or the library's static scratch (the
+// no-allocation entry point), which must hold what the plan actually uses.
+struct BwdScratch {
+    bool is_static = false;
+};
+
 template <bool RMS>
 static norm_status bwd_entry(norm_dtype dt, int64_t M, int64_t N, const void *dy, const void *x,
                              const void *w, const float *mean, const float *rstd, void *dx,
-                             void *dw, void *db, void *ws, size_t ws_bytes, void *stream) {
+                             void *dw, void *db, void *ws, size_t ws_bytes, void *stream,
+                             BwdScratch scratch_mode = {}) {
     CallScope scope;
     norm_status st = check_rows(dt, M, N);
     if (st != NORM_OK) return st;
@@ -181,8 +224,10 @@ static norm_status bwd_entry(norm_dtype dt, int64_t M, int64_t N, const void *dy
         if (M > 0) return NORM_ERR_NULL;
     }
     const bool want = dw || db;
-    const size_t need = want ? bwd_ws_bytes(dt, M, N, RMS ? 1 : 2) : 0;
-    if (want && (ws == nullptr || ws_bytes < need)) return NORM_ERR_WORKSPACE;
+    if (!scratch_mode.is_static) {
+        const size_t need = want ? bwd_ws_bytes(dt, M, N, RMS ? 1 : 2) : 0;
+        if (want && (ws == nullptr || ws_bytes < need)) return NORM_ERR_WORKSPACE;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int n = (int)N;
     if (M == 0) {
@@ -203,9 +248,20 @@ static norm_status bwd_entry(norm_dtype dt, int64_t M, int64_t N, const void *dy
     // One block: it writes dw / db directly.  Otherwise float32 partial
     // rows in the workspace, added by the column-sum kernel.
     const bool direct = p.grid == 1;
+    size_t part_stride = (size_t)max_partial_rows(M) * N;  // floats from part_w to part_b
+    if (scratch_mode.is_static) {
+        // The static scratch holds exactly the partial rows this plan
+        // writes; a shape that needs more is refused before anything runs.
+        part_stride = (size_t)p.grid * N;
+        const size_t used = (want && !direct) ? part_stride * sizeof(float) * (RMS ? 1 : 2) : 0;
+        if (used > kScratchBytes) return NORM_ERR_WORKSPACE;
+        if (used) {
+            ws = static_scratch();
+            if (!ws) return NORM_ERR_HIP;
+        }
+    }
     float *part_w = (dw && !direct) ? static_cast<float *>(ws) : nullptr;
-    float *part_b = (!RMS && db && !direct) ? static_cast<float *>(ws) + (size_t)max_partial_rows(M) * N
-                                            : nullptr;
+    float *part_b = (!RMS && db && !direct) ? static_cast<float *>(ws) + part_stride : nullptr;
     void *dw_out = direct ? dw : nullptr;
     void *db_out = (direct && !RMS) ? db : nullptr;
     return with_io_type(dt, [&](auto tag) {
@@ -254,4 +310,10 @@ extern "C" norm_status rms_bwd(norm_dtype dt, int64_t M, int64_t N, const void *
                                const void *w, const float *rstd, void *dx, void *dw, void *ws,
                                size_t ws_bytes, void *stream) {
     return bwd_entry<true>(dt, M, N, dy, x, w, nullptr, rstd, dx, dw, nullptr, ws, ws_bytes, stream);
+}
+
+extern "C" norm_status rms_bwd_noalloc(norm_dtype dt, int64_t M, int64_t N, const void *dy, const void *x,
+                                       const void *w, const float *rstd, void *dx, void *dw, void *stream) {
+    return bwd_entry<true>(dt, M, N, dy, x, w, nullptr, rstd, dx, dw, nullptr, nullptr, 0, stream,
+                           BwdScratch{true});
 }

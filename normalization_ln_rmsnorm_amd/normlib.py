@@ -39,6 +39,7 @@ SIGNATURES = {
     "rms_fwd": (_I, [_I, _I64, _I64, _F, _V, _V, _V, _V, _V]),
     "rms_bwd_workspace_bytes": (_SZ, [_I, _I64, _I64]),
     "rms_bwd": (_I, [_I, _I64, _I64, _V, _V, _V, _V, _V, _V, _V, _SZ, _V]),
+    "rms_bwd_noalloc": (_I, [_I, _I64, _I64, _V, _V, _V, _V, _V, _V, _V]),
     "bn_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64]),
     "bn_fwd_train": (_I, [_I, _I64, _I64, _I64, _F, _F, _I, _F, _V, _V, _V, _V, _V, _V, _V, _V,
                           _V, _V, _SZ, _V]),
@@ -226,6 +227,19 @@ def rms_bwd(dy, x, w, rstd, *, want_dw=True, dx=None, dw=None, ws=None):
     ws, nbytes = _workspace(need, x.device, ws)
     _check("rms_bwd", lib().rms_bwd(_dt(x), M, N, _ptr(dy), _ptr(x), _ptr(w), _ptr(rstd), _ptr(dx),
                                     _ptr(dw), _ptr(ws), nbytes, _stream(x.device)))
+    return dx, dw
+
+
+def rms_bwd_noalloc(dy, x, w, rstd, *, dx, dw=None):
+    """rms_bwd through the entry point that allocates nothing (the dw partial
+    rows live in the library's static per-GPU scratch).  dx (and dw, if
+    wanted) must be passed in; nothing is allocated here either.  Calls that
+    overlap on one GPU race on the scratch.  Returns (dx, dw)."""
+    N = x.shape[-1]
+    M = x.numel() // N if N else 0
+    _same(dy, x, "dy"); _same(w, x, "w"); _same(dx, x, "dx"); _same(dw, x, "dw")
+    _check("rms_bwd_noalloc", lib().rms_bwd_noalloc(_dt(x), M, N, _ptr(dy), _ptr(x), _ptr(w), _ptr(rstd),
+                                                    _ptr(dx), _ptr(dw), _stream(x.device)))
     return dx, dw
 
 

@@ -202,3 +202,16 @@ def test_regular_build_reads_no_environment():
                          text=True, check=True).stdout
     imported = set(line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip())
     assert "getenv" not in imported and "secure_getenv" not in imported
+
+
+def test_noalloc_entry_point_validation(lib):
+    """rms_bwd_noalloc checks its arguments like rms_bwd, and refuses a shape
+    whose partial rows exceed the static scratch before touching the GPU."""
+    f = lib.rms_bwd_noalloc
+    assert f(3, 4, 8, P, P, P, P, P, P, NULL) == EDTYPE
+    assert f(BF16, 4, 0, P, P, P, P, P, P, NULL) == ESHAPE
+    assert f(BF16, 4, 8, NULL, P, P, P, P, P, NULL) == ENULL
+    assert f(BF16, 4, 8, P, P, P, NULL, P, P, NULL) == ENULL
+    assert f(BF16, 8192, 16384, P, P, P, P, P, P, NULL) == EWS
+    assert f(F32, 8192, 32768, P, P, P, P, P, P, NULL) == EWS
+    assert f(BF16, 0, 8, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == OK

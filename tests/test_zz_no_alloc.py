@@ -1,0 +1,59 @@
+"""rms_bwd_noalloc (the entry point that allocates nothing; its dw partial
+rows live in the library's static per-GPU scratch) against rms_bwd (caller
+workspace), through the C ABI: two calls in a row, the second smaller, each
+compared with the regular entry point bit for bit and with the float64
+oracle at the bf16 tolerance; shapes beyond the scratch are refused."""
+import numpy as np
+import pytest
+import torch
+
+from tests._parity import Guarded, assert_guards, check, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+nl = pytest.importorskip("normalization_ln_rmsnorm_amd")
+from normalization_ln_rmsnorm_amd.workloads import WORKLOADS, gen_rowwise  # noqa: E402
+
+WL = WORKLOADS["rms_bf16_16384x4096"]
+
+
+def _one(orc, M, N):
+    inp = gen_rowwise(WL, M=M, N=N)
+    x, dy, w = (to_dev(inp[k], "bf16") for k in ("x", "dy", "w"))
+    _, rstd = nl.rms_fwd(x, w, WL.eps)
+    dx_ref, dw_ref = nl.rms_bwd(dy, x, w, rstd)
+    G = dict(dx=Guarded((M, N), torch.bfloat16), dw=Guarded((N,), torch.bfloat16))
+    dx, dw = nl.rms_bwd_noalloc(dy, x, w, rstd, dx=G["dx"].t, dw=G["dw"].t)
+    assert_guards(G)
+    assert torch.equal(dx.view(torch.int16), dx_ref.view(torch.int16))
+    assert torch.equal(dw.view(torch.int16), dw_ref.view(torch.int16))
+    rdx, rdw = orc.rms_bwd(inp["dy"], inp["x"], inp["w"], eps=WL.eps, bf16=True)
+    g = np.abs(orc.widen(inp["dy"], bf16=True) * orc.widen(inp["w"], bf16=True))
+    _, rr = orc.rms_fwd(inp["x"], inp["w"], eps=WL.eps, bf16=True)
+    check(f"noalloc {M}x{N} dx", to_f64(dx), rdx, "bf16", group_axis=1,
+          scale=rr[:, None] * g.max(axis=1, keepdims=True))
+    check(f"noalloc {M}x{N} dw", to_f64(dw), rdw, "bf16")
+
+
+def test_two_calls_second_smaller(orc):
+    """The full RMSNorm workload shape, then a smaller one (fewer partial
+    rows and a narrower row): the scratch keeps the first call's contents,
+    which the second must not pick up."""
+    print("case noalloc 16384x4096 then 3000x1024", flush=True)
+    _one(orc, 16384, 4096)
+    _one(orc, 3000, 1024)
+    torch.cuda.synchronize()
+
+
+def test_shape_beyond_the_scratch_is_refused():
+    """N = 16384 with many rows needs 512 partial rows of 64 KiB: more than
+    the scratch; refused before any launch (outputs untouched)."""
+    M, N = 8192, 16384
+    x = torch.zeros(M, N, dtype=torch.bfloat16, device="cuda")
+    rstd = torch.ones(M, device="cuda")
+    dx = torch.full_like(x, 7.0)
+    dw = torch.full((N,), 7.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(nl.NormError, match="NORM_ERR_WORKSPACE"):
+        nl.rms_bwd_noalloc(x, x, None, rstd, dx=dx, dw=dw)
+    torch.cuda.synchronize()
+    assert bool((dx == 7.0).all()) and bool((dw == 7.0).all())
