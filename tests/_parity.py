@@ -111,6 +111,10 @@ def to_io(a, dtype):
     return _to_io(a, dtype)
 
 
+# Elements moved off a kink / decided by the GPU's side, per case; the test
+# session prints them at the end (tests/conftest.py).
+KINK_LOG = []
+
 # ------------------------------------------------------------- guard bands
 # Every output a GPU test checks sits inside a larger buffer whose GUARD
 # elements on each side hold a fixed NaN bit pattern; after the call the

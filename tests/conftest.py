@@ -18,3 +18,17 @@ def orc():
     import oracle
     oracle._load()
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Kink bookkeeping of the BatchNorm parity cases: how many elements
+    were moved off an activation kink, or decided by the GPU's own side on
+    unedited inputs."""
+    try:
+        from tests._parity import KINK_LOG
+    except Exception:
+        return
+    if KINK_LOG:
+        terminalreporter.write_sep("-", "activation kinks in the parity inputs")
+        for line in KINK_LOG:
+            terminalreporter.write_line(line)
