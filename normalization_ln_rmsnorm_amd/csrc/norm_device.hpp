@@ -321,18 +321,23 @@ __device__ __forceinline__ float gelu_grad_exact(float z) {
 
 // Fast GELU'(z) (FAST = true).  With e = exp(-z^2 / 2) and Phi(-|z|) =
 // P(t) t e (the halved 7.1.26 polynomial P, t = 1 / (1 + p |z| / sqrt 2)):
-// Phi(z) = H(z) - s P(t) t e with H = 1, s = 1 for z >= 0 and H = 0, s = -1
-// below, so GELU'(z) = H + e (z / sqrt(2 pi) - s P(t) t): the sign, the two
-// products with e and the final add fold into two FMAs.
+// Phi(z) = H(z) - s P(t) t e with s = sign(z) and H = (1 + s) / 2 (1 for
+// z >= 0, 0 below), so GELU'(z) = H + e (z / sqrt(2 pi) - P(t) s t).  The
+// sign rides in the reciprocal: s t = 1 / (s + p z / sqrt 2) (both terms
+// carry the sign of z), and P takes |s t| = t through the operand's
+// absolute-value modifier; s itself is one bit-select (copysign), H one
+// FMA.  That replaces the compare and the two selects of the plain form.
+__device__ __forceinline__ float sign_of(float v) { return __builtin_copysignf(1.0f, v); }
 __device__ __forceinline__ float gelu_grad_fast(float z) {
     const float e = __builtin_amdgcn_exp2f(z * z * kNegHalfLog2e);
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * kInvSqrt2, fabsf(z), 1.0f));
+    const float sg = sign_of(z);
+    const float st = __builtin_amdgcn_rcpf(fmaf(0.3275911f * kInvSqrt2, z, sg));  // s t
+    const float t = fabsf(st);
     float p = fmaf(t, 0.5307027145f, -0.7265760135f);
     p = fmaf(t, p, 0.7107068705f);
     p = fmaf(t, p, -0.142248368f);
     p = fmaf(t, p, 0.127414796f);
-    const bool pos = z >= 0.0f;
-    return fmaf(e, fmaf(pos ? -p : p, t, z * kInvSqrt2Pi), pos ? 1.0f : 0.0f);
+    return fmaf(e, fmaf(-p, st, z * kInvSqrt2Pi), fmaf(0.5f, sg, 0.5f));
 }
 
 // gelu_grad_fast of z = w / kGeluWScale.  A caller that forms z as x a + s
@@ -342,13 +347,14 @@ __device__ __forceinline__ float gelu_grad_fast(float z) {
 constexpr float kGeluWScale = 0.84932180f;
 __device__ __forceinline__ float gelu_grad_fast_w(float w) {
     const float e = __builtin_amdgcn_exp2f(-w * w);
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.27273747f, fabsf(w), 1.0f));  // p / sqrt 2 / kGeluWScale
+    const float sg = sign_of(w);
+    const float st = __builtin_amdgcn_rcpf(fmaf(0.27273747f, w, sg));  // p / sqrt 2 / kGeluWScale
+    const float t = fabsf(st);
     float p = fmaf(t, 0.5307027145f, -0.7265760135f);
     p = fmaf(t, p, 0.7107068705f);
     p = fmaf(t, p, -0.142248368f);
     p = fmaf(t, p, 0.127414796f);
-    const bool pos = w >= 0.0f;
-    return fmaf(e, fmaf(pos ? -p : p, t, w * 0.46971864f), pos ? 1.0f : 0.0f);  // 1 / sqrt(2 pi) / kGeluWScale
+    return fmaf(e, fmaf(-p, st, w * 0.46971864f), fmaf(0.5f, sg, 0.5f));  // 1 / sqrt(2 pi) / kGeluWScale
 }
 
 // Fast forward GELU (FAST = true).  The forward needs Phi but not phi, so it

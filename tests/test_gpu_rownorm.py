@@ -215,13 +215,18 @@ def test_empty_batch_is_noop(orc):
 
 @pytest.mark.parametrize("kind", ["ln", "rms"])
 def test_rows_past_2_32_elements(orc, kind):
-    """bf16, 2^20 + 64 rows x 4096 (2^32 + 2^18 elements, 8 GiB per tensor):
-    every element index of the row path beyond 32 bits.  Rows are
-    independent, so a 64-row block repeated down the rows has the oracle's
+    """bf16, 63 x 16646 = 1048698 rows x 4096 (past 2^32 elements, 8 GiB per
+    tensor): every element index of the row path beyond 32 bits.  Rows are
+    independent, so a 63-row block repeated down the rows has the oracle's
     block outputs in every copy; each output is checked through its maximum
     and minimum over the copies (both within tolerance bound every copy),
-    and dw / db, which add the copies, per copy."""
-    dtype, N, B, reps = "bf16", 4096, 64, (1 << 14) + 1
+    and dw / db, which add the copies, per copy.  The period is odd on
+    purpose: with a power-of-two period dividing the persistent grid's row
+    step, every block would add the same two rows thousands of times and
+    its float32 partial of dw would repeat one rounding coherently (a
+    property of that adversarial input, not of the index arithmetic under
+    test); an odd period gives every block varied rows, as data does."""
+    dtype, N, B, reps = "bf16", 4096, 63, 16646
     wl = _wl(kind, dtype)
     inp = gen_rowwise(wl, M=B, N=N)
     x = to_dev(inp["x"], dtype).repeat(reps, 1)
@@ -276,3 +281,31 @@ def test_f32_rows_far_from_zero(orc, M, N):
     inp["x"] = (inp["x"].astype(np.float64) + off[:, None]).astype(np.float32)
     print(f"case ln f32 far-from-zero {M}x{N}", flush=True)
     run_case(orc, "ln", "f32", M, N, inp=inp)
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
+def test_workspace_reused_across_shapes(orc, kind):
+    """One workspace through backward calls of alternating shapes and data:
+    every call's dw / db must come from its own partial rows, never from
+    rows an earlier call left in the workspace (or in a cache)."""
+    dtype, N = "bf16", 4096
+    wl = _wl(kind, dtype)
+    need = (nl.ln_bwd_workspace_bytes if kind == "ln" else nl.rms_bwd_workspace_bytes)(
+        torch.bfloat16, 8192, N)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    cases = [(8192, 11), (2048, 12), (6000, 13), (2048, 14), (8192, 15), (777, 16)]
+    print(f"case {kind} ws reuse {cases}", flush=True)
+    for M, seed in cases:
+        inp = gen_rowwise(wl, M=M, N=N, seed=seed)
+        x, dy, w = (to_dev(inp[k], dtype) for k in ("x", "dy", "w"))
+        if kind == "ln":
+            b = to_dev(inp["b"], dtype)
+            _, mean, rstd = nl.ln_fwd(x, w, b, wl.eps)
+            _, dw, db = nl.ln_bwd(dy, x, w, mean, rstd, ws=ws)
+            _, rdw, rdb = orc.ln_bwd(inp["dy"], inp["x"], inp["w"], eps=wl.eps, bf16=True)
+            check(f"{kind} reuse {M} db", to_f64(db), rdb, dtype)
+        else:
+            _, rstd = nl.rms_fwd(x, w, wl.eps)
+            _, dw = nl.rms_bwd(dy, x, w, rstd, ws=ws)
+            _, rdw = orc.rms_bwd(inp["dy"], inp["x"], inp["w"], eps=wl.eps, bf16=True)
+        check(f"{kind} reuse {M} dw", to_f64(dw), rdw, dtype)
