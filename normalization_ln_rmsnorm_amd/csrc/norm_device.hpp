@@ -173,6 +173,20 @@ __device__ __forceinline__ void vstore_out(T *base, uint32_t idx, const typename
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)r, store_rsrc(base), off, 0, kStoreCachePolicy);
 }
 
+// Range-checked 16-byte loads through a raw buffer resource of `bytes`
+// bytes over `base` (the same in every lane): a lane whose byte offset lies
+// outside the range reads zeros, so bounds need no branch per load.  Lanes
+// that must read zeros pass kOffNone, far past any range used here.
+constexpr uint32_t kOffNone = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t load_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+// POLICY: 0 for data read again (w, b), 2 (non-temporal) for streams.
+template <int POLICY>
+__device__ __forceinline__ u32x4 vload16_rsrc(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, POLICY);
+}
+
 // Scalar parameter load (w, b, statistics) widened to float.
 __device__ __forceinline__ float ld1(const float *p) { return *p; }
 __device__ __forceinline__ float ld1(const bf16_t *p) { return __uint_as_float(uint32_t(p->bits) << 16); }

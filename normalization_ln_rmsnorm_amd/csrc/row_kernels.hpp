@@ -95,7 +95,10 @@ template <typename R> __device__ __forceinline__ void opaque(R &r) { asm volatil
 // deviations (exact two-pass over the register-resident row), rstd by rsqrt,
 // y = (x - mean) * rstd * w + b.  RMSNorm ([NormPage] "RMSNorm" section):
 // no mean; rstd from the mean of squares; y = x * rstd * w.
-template <typename T, int V, int IT, bool RMS, int MAXB>
+// ONE: the grid gives every block exactly one row group (the default
+// plan); the kernel then neither loops nor holds a prefetched next row,
+// which frees IT vectors of registers per thread for more waves per CU.
+template <typename T, int V, int IT, bool RMS, int MAXB, bool ONE>
 __global__ void __launch_bounds__(MAXB)
 row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ b,
                T *__restrict__ y, float *__restrict__ mean_out, float *__restrict__ rstd_out,
@@ -109,24 +112,71 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
     const int rpb = blockDim.x / tpr;
     const int slot_in_block = threadIdx.x / tpr;
 
-    raw_t wr[IT], br[IT];
+    // Row loop (one pass per block on the default, non-persistent grid; more
+    // on a persistent grid).  The next row's loads are issued before this
+    // row is reduced and stored.
+    const int64_t step = (int64_t)gridDim.x * rpb;
+    int64_t base = (int64_t)blockIdx.x * rpb;
+
+    // x of the row group starting at row `gbase`, this thread's slots.  On
+    // the 16-byte path a buffer resource spans the group's rows, so lanes
+    // past the last row or past the row's end read zeros without a branch:
+    // branches around the loads made the compiler wait for each load before
+    // issuing the next.  The group spans at most 1024 x 8 x 8 elements, so
+    // its byte offsets fit 32 bits.
+    auto load_group = [&](raw_t *dst, int64_t gbase) {
+        if constexpr (sizeof(raw_t) == 16) {
+            const int64_t rows = gbase < M ? (M - gbase < rpb ? M - gbase : (int64_t)rpb) : 0;
+            const auto rs = load_rsrc(rows ? x + gbase * N : x, (uint32_t)(rows * N * (int64_t)sizeof(T)));
 #pragma unroll
-    for (int k = 0; k < IT; ++k) {
-        const int v = lane + k * tpr;
-        wr[k] = ones_raw<VT>();
-        br[k] = zeros_raw<VT>();
-        if (v < nv) {
-            if (w) wr[k] = vload<T, V>(w + (int64_t)v * V);
-            if (!RMS && b) br[k] = vload<T, V>(b + (int64_t)v * V);
+            for (int k = 0; k < IT; ++k) {
+                const int v = lane + k * tpr;
+                const uint32_t off =
+                    v < nv ? (uint32_t)(((int64_t)slot_in_block * N + (int64_t)v * V) * (int64_t)sizeof(T)) : kOffNone;
+                dst[k] = vload16_rsrc<2>(rs, off);
+            }
+        } else {
+            const int64_t row = gbase + slot_in_block;
+#pragma unroll
+            for (int k = 0; k < IT; ++k) {
+                const int v = lane + k * tpr;
+                dst[k] = zeros_raw<VT>();
+                if (row < M && v < nv) dst[k] = vload_stream<T, V>(x + row * N + (int64_t)v * V);
+            }
+        }
+    };
+    raw_t xr[IT];
+    load_group(xr, base);
+
+    raw_t wr[IT], br[IT];
+    if constexpr (sizeof(raw_t) == 16) {
+        // A null w or b gets an empty range (its loads read zeros); a null w
+        // then becomes all ones through the fill pattern, with no branch.
+        const uint32_t pbytes = (uint32_t)(N * (int64_t)sizeof(T));
+        const auto rw = load_rsrc(w, w ? pbytes : 0u);
+        const auto rb = load_rsrc(b, b ? pbytes : 0u);
+        const raw_t wfill = w ? zeros_raw<VT>() : ones_raw<VT>();
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int v = lane + k * tpr;
+            const uint32_t off = v < nv ? (uint32_t)v * 16u : kOffNone;
+            wr[k] = vload16_rsrc<0>(rw, off) | wfill;
+            br[k] = zeros_raw<VT>();
+            if constexpr (!RMS) br[k] = vload16_rsrc<0>(rb, off);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < IT; ++k) {
+            const int v = lane + k * tpr;
+            wr[k] = ones_raw<VT>();
+            br[k] = zeros_raw<VT>();
+            if (v < nv) {
+                if (w) wr[k] = vload<T, V>(w + (int64_t)v * V);
+                if (!RMS && b) br[k] = vload<T, V>(b + (int64_t)v * V);
+            }
         }
     }
 
-    // Row loop (one pass per block on the default, non-persistent grid; more
-    // on a persistent grid).  The next row's loads are issued before this
-    // row is reduced and stored; they sit under bounds branches, so the
-    // compiler waits for all outstanding loads before the row's first pass.
-    const int64_t step = (int64_t)gridDim.x * rpb;
-    int64_t base = (int64_t)blockIdx.x * rpb;
     // LDS slot of the sum of squares.  A row spanning several waves reads
     // every wave's partial after one barrier; a fast wave may reach the next
     // row's write before a slow one has read this row's partials, so two
@@ -134,27 +184,11 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
     // (mean) then 1 (squares) in every row, RMSNorm alternates its single
     // reduction between the slots from row to row.
     int qslot = 1;
-    raw_t xr[IT];
-    {
-        const int64_t row = base + slot_in_block;
-#pragma unroll
-        for (int k = 0; k < IT; ++k) {
-            const int v = lane + k * tpr;
-            xr[k] = zeros_raw<VT>();
-            if (row < M && v < nv) xr[k] = vload_stream<T, V>(x + row * N + (int64_t)v * V);
-        }
-    }
     for (; base < M; base += step) {
         const int64_t row = base + slot_in_block;
         const bool active = row < M;
-        const int64_t nrow = row + step;
         raw_t nx[IT];
-#pragma unroll
-        for (int k = 0; k < IT; ++k) {
-            const int v = lane + k * tpr;
-            nx[k] = zeros_raw<VT>();
-            if (nrow < M && v < nv) nx[k] = vload_stream<T, V>(x + nrow * N + (int64_t)v * V);
-        }
+        if constexpr (!ONE) load_group(nx, base + step);
 #pragma unroll
         for (int k = 0; k < IT; ++k) {  // keep w, b packed (no hoisted float copies)
             opaque(wr[k]);
@@ -191,16 +225,28 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
 #pragma unroll
             for (int k = 0; k < IT; ++k) opaque(xr[k]);
         }
+        // Slots past the row's end hold zeros: they add nothing for RMSNorm
+        // but mean^2 for LayerNorm, so LayerNorm masks them, only in a slice
+        // k that reaches past the row's end (a uniform test: full slices
+        // skip the per-element select).
         float q = 0.0f;
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
-            const bool valid = lane + k * tpr < nv;
             float f[V];
             VT::unpack(xr[k], f);
+            if (RMS || (k + 1) * tpr <= nv) {
 #pragma unroll
-            for (int e = 0; e < V; ++e) {
-                const float d = f[e] - mean;
-                q += valid ? d * d : 0.0f;
+                for (int e = 0; e < V; ++e) {
+                    const float d = f[e] - mean;
+                    q += d * d;
+                }
+            } else {
+                const bool valid = lane + k * tpr < nv;
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float d = f[e] - mean;
+                    q += valid ? d * d : 0.0f;
+                }
             }
         }
         const float rstd = rsqrtf(row_sum(q, tpr, lds, qslot) * inv_n + eps);
@@ -228,6 +274,7 @@ row_fwd_kernel(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
                 if (rstd_out) rstd_out[row] = rstd;
             }
         }
+        if constexpr (ONE) break;
 #pragma unroll
         for (int k = 0; k < IT; ++k) xr[k] = nx[k];
     }
@@ -524,17 +571,23 @@ norm_status row_launch_fwd(const RowPlan &p, hipStream_t s, const void *x, const
     using fn_t = void (*)(const T *, const T *, const T *, T *, float *, float *, int64_t, int,
                           float, float, int);
     fn_t fn = nullptr;
+    const int64_t rpb = p.block / p.tpr;
+    const bool one = (int64_t)p.grid * rpb >= M;  // every block one row group
+#define MI355NORM_FWD(IT)                                                                              \
+    (p.block > 256 ? (one ? row_fwd_kernel<T, V, IT, RMS, 1024, true> : row_fwd_kernel<T, V, IT, RMS, 1024, false>) \
+                   : (one ? row_fwd_kernel<T, V, IT, RMS, 256, true> : row_fwd_kernel<T, V, IT, RMS, 256, false>))
     switch (p.it) {
-    case 1: fn = p.block > 256 ? row_fwd_kernel<T, V, 1, RMS, 1024> : row_fwd_kernel<T, V, 1, RMS, 256>; break;
-    case 2: fn = p.block > 256 ? row_fwd_kernel<T, V, 2, RMS, 1024> : row_fwd_kernel<T, V, 2, RMS, 256>; break;
-    case 3: if constexpr (V > 1) fn = p.block > 256 ? row_fwd_kernel<T, V, 3, RMS, 1024> : row_fwd_kernel<T, V, 3, RMS, 256>; break;
-    case 4: fn = p.block > 256 ? row_fwd_kernel<T, V, 4, RMS, 1024> : row_fwd_kernel<T, V, 4, RMS, 256>; break;
-    case 6: if constexpr (V > 1) fn = p.block > 256 ? row_fwd_kernel<T, V, 6, RMS, 1024> : row_fwd_kernel<T, V, 6, RMS, 256>; break;
-    case 8: fn = p.block > 256 ? row_fwd_kernel<T, V, 8, RMS, 1024> : row_fwd_kernel<T, V, 8, RMS, 256>; break;
-    case 16: if constexpr (V == 1) fn = p.block > 256 ? row_fwd_kernel<T, V, 16, RMS, 1024> : row_fwd_kernel<T, V, 16, RMS, 256>; break;
-    case 32: if constexpr (V == 1) fn = p.block > 256 ? row_fwd_kernel<T, V, 32, RMS, 1024> : row_fwd_kernel<T, V, 32, RMS, 256>; break;
-    case 64: if constexpr (V == 1) fn = p.block > 256 ? row_fwd_kernel<T, V, 64, RMS, 1024> : row_fwd_kernel<T, V, 64, RMS, 256>; break;
+    case 1: fn = MI355NORM_FWD(1); break;
+    case 2: fn = MI355NORM_FWD(2); break;
+    case 3: if constexpr (V > 1) fn = MI355NORM_FWD(3); break;
+    case 4: fn = MI355NORM_FWD(4); break;
+    case 6: if constexpr (V > 1) fn = MI355NORM_FWD(6); break;
+    case 8: fn = MI355NORM_FWD(8); break;
+    case 16: if constexpr (V == 1) fn = MI355NORM_FWD(16); break;
+    case 32: if constexpr (V == 1) fn = MI355NORM_FWD(32); break;
+    case 64: if constexpr (V == 1) fn = MI355NORM_FWD(64); break;
     }
+#undef MI355NORM_FWD
     if (!fn) return NORM_ERR_SHAPE;
     launch(RMS ? "row_fwd_kernel<rms>" : "row_fwd_kernel<ln>", true, fn, dim3(p.grid), dim3(p.block), 0, s,
            (const T *)x, (const T *)w, (const T *)b, (T *)y, mean, rstd, M, N, 1.0f / (float)N, eps, p.tpr);
