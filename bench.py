@@ -288,7 +288,7 @@ class AdBench:
         self.dominant = "bwd"
 
     def cpu_units(self):
-        """Blocks of 2^16 elements (offsets stay multiples of 4)."""
+        """Blocks of 2^16 elements (offsets stay multiples of 8)."""
         return -(-self.x.numel() // (1 << 16))
 
     def cpu_prepare(self, orc, u0, u1):

@@ -240,15 +240,16 @@ norm_status bn_bwd(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW,
  * -- in one pass over x; the backward recomputes the same mask from (seed,
  * offset) and returns dx = keep ? dy * act'(x) / (1-p) : 0.  Element-wise
  * over n contiguous elements of x, y, dy, dx (dtype dt).
- * Mask: element e = offset + i takes word e mod 4 of Philox4x32-10
- * (Salmon et al., SC 2011) with key (seed mod 2^32, seed / 2^32) and
- * counter ((e/4) mod 2^32, (e/4) / 2^32, 0, 0); it is dropped iff
- * (word >> 8) < round(p * 2^24).  Calls with the same (seed, offset, n)
+ * Mask: element e = offset + i takes 16 bits of Philox4x32-10 (Salmon et
+ * al., SC 2011) with key (seed mod 2^32, seed / 2^32) and counter
+ * ((e/8) mod 2^32, (e/8) / 2^32, 0, 0): word (e mod 8)/2, its low half for
+ * even e, its high half for odd e; it is dropped iff those 16 bits are
+ * below round(p * 2^16) (p on a grid of 2^-16).  Calls with the same (seed, offset, n)
  * give the same mask; splitting a tensor across calls with offsets keeps
  * the whole-tensor mask.
  *   act, act_param  as for BatchNorm (the activation and its parameter)
  *   drop_p          in [0, 1]; 0 gives the plain activation, 1 all zeros
- *   offset          a multiple of 4 (NORM_ERR_ARG otherwise), offset + n
+ *   offset          a multiple of 8 (NORM_ERR_ARG otherwise), offset + n
  *                   must not overflow 64 bits
  * n = 0 is a no-op. */
 norm_status act_dropout_fwd(norm_dtype dt, int64_t n, norm_act act, float act_param,

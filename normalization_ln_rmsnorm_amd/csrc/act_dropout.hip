@@ -13,13 +13,13 @@
 
 namespace mi355norm {
 
-// Drop threshold on the top 24 bits of a generator word: round(p * 2^24),
-// 0 for p = 0 and 2^24 (drop everything) for p = 1.
+// Drop threshold on an element's 16 generator bits: round(p * 2^16), 0 for
+// p = 0 and 2^16 (drop everything) for p = 1.
 static uint32_t drop_threshold(float p) {
     const double d = (double)p;
     if (!(d > 0.0)) return 0u;
-    if (d >= 1.0) return 1u << 24;
-    return (uint32_t)floor(d * 16777216.0 + 0.5);
+    if (d >= 1.0) return 1u << 16;
+    return (uint32_t)floor(d * 65536.0 + 0.5);
 }
 
 static norm_status check_ad(norm_dtype dt, int64_t n, norm_act act, float act_param, float drop_p,
@@ -29,7 +29,7 @@ static norm_status check_ad(norm_dtype dt, int64_t n, norm_act act, float act_pa
     if (!act_ok(act)) return NORM_ERR_ACT;
     if (!act_param_ok(act, act_param)) return NORM_ERR_ARG;
     if (!(drop_p >= 0.0f && drop_p <= 1.0f)) return NORM_ERR_ARG;
-    if (offset % 4 != 0) return NORM_ERR_ARG;
+    if (offset % 8 != 0) return NORM_ERR_ARG;
     if (offset > UINT64_MAX - (uint64_t)n) return NORM_ERR_ARG;
     return NORM_OK;
 }
@@ -40,7 +40,7 @@ static AdArgs make_args(int64_t n, norm_act act, float act_param, float drop_p, 
     a.n = n;
     a.k0 = (uint32_t)seed;
     a.k1 = (uint32_t)(seed >> 32);
-    a.blk0 = offset >> 2;
+    a.blk0 = offset >> 3;
     a.thresh = drop_threshold(drop_p);
     a.scale = drop_p < 1.0f ? 1.0f / (1.0f - drop_p) : 0.0f;
     a.act_rt = (int)act;

@@ -8,17 +8,19 @@
 //             recomputed in the backward instead of stored) and 6 (one
 //             kernel per activation, the rest pruned at compile time).
 //
-// Mask.  Element e (the caller's offset, a multiple of 4, plus the flat
-// index) takes word e mod 4 of Philox4x32-10 (Salmon et al., SC 2011) under
-// key (seed low, seed high) and counter (e / 4 low, e / 4 high, 0, 0): one
-// generator call yields the words of four consecutive elements, so a
-// float32 vector costs one call and a 16-bit vector two.  The element is
-// dropped when (word >> 8) < thresh (thresh / 2^24 is the drop
-// probability); survivors are scaled by 1 / (1 - p).
+// Mask.  Element e (the caller's offset, a multiple of 8, plus the flat
+// index) takes 16 bits of Philox4x32-10 (Salmon et al., SC 2011) under key
+// (seed low, seed high) and counter (e / 8 low, e / 8 high, 0, 0): word
+// (e mod 8) / 2, its low half for even e, its high half for odd e.  One
+// generator call serves eight consecutive elements, one 16-bit vector (a
+// float32 vector uses half a call).  The element is dropped when its 16
+// bits are below thresh (thresh / 2^16 is the drop probability); survivors
+// are scaled by 1 / (1 - p).
 //
 // Both directions are bound by HBM traffic (2 tensors forward, 3 backward);
-// the ten Philox rounds cost ~20 VALU operations per element, a fraction of
-// the VALU budget at 8 TB/s.
+// the ten Philox rounds are 20 64-bit multiplies and 40 XORs per call, so
+// taking 16 bits per element (one call per 16-bit vector, not two) is what
+// keeps the 16-bit GELU forward near the HBM rate.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -37,8 +39,8 @@ constexpr int kAdUnroll = 4;  // vectors per thread
 struct AdArgs {
     int64_t n;           // elements
     uint32_t k0, k1;     // Philox key (seed)
-    uint64_t blk0;       // offset / 4: the counter of element 0's word group
-    uint32_t thresh;     // drop when (word >> 8) < thresh
+    uint64_t blk0;       // offset / 8: the counter of element 0's group
+    uint32_t thresh;     // drop when the element's 16 bits are below thresh
     float scale;         // 1 / (1 - p)
     int act_rt;          // activation for the run-time dispatched instance
     float act_p;         // its parameter
@@ -72,24 +74,34 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
     w[3] = c3;
 }
 
-// Keep flags of the V elements of vector vi (V = 4 or 8), or of element vi
+// The 16 bits of word w that element parity `odd` takes.
+__device__ __forceinline__ uint32_t half16(uint32_t w, bool odd) { return odd ? (w >> 16) : (w & 0xffffu); }
+
+// Keep flags of the V elements of vector vi (V = 8 or 4), or of element vi
 // for V = 1.
 template <int V>
 __device__ __forceinline__ void keep_flags(const AdArgs &a, int64_t vi, bool keep[V]) {
-    if constexpr (V == 1) {
-        const uint64_t blk = a.blk0 + (uint64_t)(vi >> 2);
-        uint32_t w[4];
+    uint32_t w[4];
+    if constexpr (V == 8) {  // elements 8 vi .. 8 vi + 7: one whole call
+        const uint64_t blk = a.blk0 + (uint64_t)vi;
         philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), a.k0, a.k1, w);
-        keep[0] = (w[vi & 3] >> 8) >= a.thresh;
-    } else {
 #pragma unroll
-        for (int g = 0; g < V / 4; ++g) {
-            const uint64_t blk = a.blk0 + (uint64_t)vi * (V / 4) + g;
-            uint32_t w[4];
-            philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), a.k0, a.k1, w);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) keep[g * 4 + e] = (w[e] >> 8) >= a.thresh;
-        }
+        for (int e = 0; e < 8; ++e) keep[e] = half16(w[e >> 1], e & 1) >= a.thresh;
+    } else if constexpr (V == 4) {  // elements 4 vi .. 4 vi + 3: words 0-1 or 2-3
+        const uint64_t blk = a.blk0 + (uint64_t)(vi >> 1);
+        philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), a.k0, a.k1, w);
+        const bool upper = vi & 1;
+        const uint32_t wa = upper ? w[2] : w[0], wb = upper ? w[3] : w[1];
+        keep[0] = half16(wa, false) >= a.thresh;
+        keep[1] = half16(wa, true) >= a.thresh;
+        keep[2] = half16(wb, false) >= a.thresh;
+        keep[3] = half16(wb, true) >= a.thresh;
+    } else {  // element vi
+        const uint64_t blk = a.blk0 + (uint64_t)(vi >> 3);
+        philox4x32_10((uint32_t)blk, (uint32_t)(blk >> 32), a.k0, a.k1, w);
+        const int q = (int)(vi & 7) >> 1;
+        const uint32_t word = q == 0 ? w[0] : q == 1 ? w[1] : q == 2 ? w[2] : w[3];
+        keep[0] = half16(word, vi & 1) >= a.thresh;
     }
 }
 

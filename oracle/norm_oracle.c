@@ -451,19 +451,26 @@ void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
     out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
 }
 
+/* The drop threshold on a 16-bit uniform: round(p * 2^16); 0 keeps every
+ * element, 2^16 drops every element. */
 uint32_t orc_dropout_threshold(double p) {
     if (!(p > 0.0)) return 0;
-    if (p >= 1.0) return 1u << 24;
-    return (uint32_t)floor(p * 16777216.0 + 0.5);
+    if (p >= 1.0) return 1u << 16;
+    return (uint32_t)floor(p * 65536.0 + 0.5);
 }
 
+/* Element e reads 16 bits of the generator: counter e / 8 yields the four
+ * words of eight consecutive elements; element e takes word (e mod 8) / 2,
+ * its low half for even e and its high half for odd e. */
 static int orc_kept(uint64_t e, uint64_t seed, uint32_t thresh) {
     const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
-    const uint64_t blk = e >> 2;
+    const uint64_t blk = e / 8;
     const uint32_t ctr[4] = {(uint32_t)blk, (uint32_t)(blk >> 32), 0u, 0u};
     uint32_t w[4];
     orc_philox4x32_10(ctr, key, w);
-    return (w[e & 3] >> 8) >= thresh;
+    const uint32_t word = w[(e % 8) / 2];
+    const uint32_t u16 = (e % 2 == 0) ? (word & 0xFFFFu) : (word >> 16);
+    return u16 >= thresh;
 }
 
 void orc_dropout_keep(int64_t n, double p, uint64_t seed, uint64_t offset, uint8_t *keep) {

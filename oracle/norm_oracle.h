@@ -93,12 +93,13 @@ void orc_bn_bwd(int64_t Nb, int64_t C, int64_t HW, double eps, int act,
  *
  * Generator: Philox4x32-10 (Salmon, Moraes, Dror & Shaw, "Parallel random
  * numbers: as easy as 1, 2, 3", SC 2011).  Element e (the caller's offset
- * plus its index) takes word e mod 4 of Philox4x32-10 with
+ * plus its index) takes 16 bits of Philox4x32-10 with
  *   key     = (seed mod 2^32, seed / 2^32)
- *   counter = ((e / 4) mod 2^32, (e / 4) / 2^32, 0, 0).
- * The element is dropped when (word >> 8) < T with T = round(p * 2^24)
- * (ties away from zero), i.e. with probability T / 2^24; a kept element is
- * scaled by 1 / (1 - p). */
+ *   counter = ((e / 8) mod 2^32, (e / 8) / 2^32, 0, 0):
+ * word (e mod 8) / 2, its low half for even e, its high half for odd e.
+ * The element is dropped when that 16-bit value u < T with
+ * T = round(p * 2^16) (ties away from zero), i.e. with probability
+ * T / 2^16; a kept element is scaled by 1 / (1 - p). */
 void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
 uint32_t orc_dropout_threshold(double p);
 /* keep[i] = 1 if element offset + i is kept, else 0. */

@@ -168,8 +168,9 @@ def test_act_dropout_errors(lib):
     assert fwd(act=10, ap=0.0) == EARG
     for bad in (-0.1, 1.5, float("nan")):
         assert fwd(p=bad) == EARG
-    assert fwd(off=2) == EARG  # the offset must be a multiple of 4
-    assert fwd(off=(1 << 64) - 4) == EARG  # offset + n overflows
+    assert fwd(off=2) == EARG  # the offset must be a multiple of 8
+    assert fwd(off=4) == EARG
+    assert fwd(off=(1 << 64) - 8) == EARG  # offset + n overflows
     assert fwd(x=NULL) == ENULL
     assert fwd(y=NULL) == ENULL
     assert fwd(n=0, x=NULL, y=NULL) == OK

@@ -65,7 +65,7 @@ def test_parity(orc, dtype, act, param, n):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("p", [0.0, 0.5, 0.9, 1.0])
-@pytest.mark.parametrize("offset", [0, 4, 1 << 34])
+@pytest.mark.parametrize("offset", [0, 8, 1 << 34])
 def test_probabilities_and_offsets(orc, dtype, p, offset):
     print(f"case act_dropout {dtype} p={p} offset={offset}", flush=True)
     if p in (0.0, 1.0):
@@ -110,7 +110,7 @@ def test_unaligned_outputs(orc, dtype, n):
     """Aligned input, outputs one element off 16-byte alignment (the scalar
     path), with guard bands."""
     print(f"case act_dropout unaligned outputs {dtype} n={n}", flush=True)
-    run_case(orc, dtype, n, "silu", 0.2, seed=11, offset=4, misalign=1)
+    run_case(orc, dtype, n, "silu", 0.2, seed=11, offset=24, misalign=1)
 
 
 def test_full_size_workload(orc):
@@ -189,7 +189,7 @@ def test_past_2_32_elements(orc):
     B, L = 1 << 20, 8192
     n = (1 << 32) + B + 3
     reps = (n - 3) // B
-    seed, off0, p = 0x5EED, 12344, 0.1  # offsets are multiples of 4
+    seed, off0, p = 0x5EED, 12344, 0.1  # offsets are multiples of 8
     inp = _inputs("bf16", B, seed=7)
     xb, dyb = to_dev(inp["x"], "bf16"), to_dev(inp["dy"], "bf16")
     x = torch.cat([xb.repeat(reps), xb[:3]])

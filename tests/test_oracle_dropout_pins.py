@@ -21,18 +21,20 @@ def test_philox_known_answers(orc):
 
 def test_threshold_rounding(orc):
     assert orc.dropout_threshold(0.0) == 0
-    assert orc.dropout_threshold(1.0) == 1 << 24
-    assert orc.dropout_threshold(0.5) == 1 << 23
-    assert orc.dropout_threshold(0.25) == 1 << 22
-    # round to nearest: 0.1 * 2^24 = 1677721.6
-    assert orc.dropout_threshold(0.1) == 1677722
+    assert orc.dropout_threshold(1.0) == 1 << 16
+    assert orc.dropout_threshold(0.5) == 1 << 15
+    assert orc.dropout_threshold(0.25) == 1 << 14
+    # round to nearest: 0.1 * 2^16 = 6553.6, 0.3 * 2^16 = 19660.8, 0.7 * 2^16 = 45875.2
+    assert orc.dropout_threshold(0.1) == 6554
+    assert orc.dropout_threshold(0.3) == 19661
+    assert orc.dropout_threshold(0.7) == 45875
 
 
 @pytest.mark.parametrize("p", [0.1, 0.5, 0.9])
 def test_keep_fraction_is_binomial(orc, p):
     n = 1 << 20
     keep = orc.dropout_keep(n, p, seed=20240611)
-    q = 1.0 - orc.dropout_threshold(p) / float(1 << 24)
+    q = 1.0 - orc.dropout_threshold(p) / float(1 << 16)
     sd = np.sqrt(q * (1 - q) / n)
     assert abs(keep.mean() - q) < 5 * sd
     # Pairs of neighbours are independent too (a stuck word would show).
@@ -90,18 +92,32 @@ def test_backward_is_the_derivative(orc, act, param):
 
 
 def test_mask_layout_known_answer(orc):
-    """Elements 0..3 under seed 0 use the four words of Philox4x32-10 at
-    counter 0 and key 0 -- the first published known-answer vector -- so
-    their keep flags at a set of thresholds are fixed by those words (a
-    different counter or word assignment changes the pattern)."""
+    """Elements 0..7 under seed 0 use the eight 16-bit halves of
+    Philox4x32-10 at counter 0 and key 0 -- the first published
+    known-answer vector -- low half first, so their keep flags at a set of
+    thresholds are fixed by those words (a different counter, word or half
+    assignment changes the pattern)."""
     kat = json.load(open(os.path.join(HERE, "golden", "philox4x32_10_kat.json")))["cases"][0]
     assert kat["ctr"] == ["00000000"] * 4 and kat["key"] == ["00000000"] * 2
-    top = [int(v, 16) >> 8 for v in kat["out"]]
-    cuts = sorted(top)
-    # thresholds below, between and above the four 24-bit values
-    ts = [0, cuts[0] // 2] + [(a + b) // 2 for a, b in zip(cuts, cuts[1:])] + [cuts[-1] + 1]
+    words = [int(v, 16) for v in kat["out"]]
+    halves = [h for w in words for h in (w & 0xFFFF, w >> 16)]
+    cuts = sorted(set(halves))
+    # thresholds below, between and above the eight 16-bit values
+    ts = [0, cuts[0] // 2] + [(a + b) // 2 + 1 for a, b in zip(cuts, cuts[1:])] + [cuts[-1] + 1]
     for t in ts:
-        p = t / float(1 << 24)
+        p = t / float(1 << 16)
         assert orc.dropout_threshold(p) == t
-        expect = np.array([1 if v >= t else 0 for v in top], dtype=np.uint8)
-        np.testing.assert_array_equal(orc.dropout_keep(4, p, seed=0, offset=0), expect)
+        expect = np.array([1 if v >= t else 0 for v in halves], dtype=np.uint8)
+        np.testing.assert_array_equal(orc.dropout_keep(8, p, seed=0, offset=0), expect)
+
+
+def test_mask_next_counter(orc):
+    """Elements 8..15 take counter 1 (the generator itself is pinned by its
+    known-answer vectors above); an offset of 8 starts at that counter."""
+    words = orc.philox4x32_10([1, 0, 0, 0], [0, 0])
+    halves = np.array([h for w in words for h in (w & 0xFFFF, w >> 16)])
+    for t in (int(np.median(halves)), int(halves.min()) + 1, int(halves.max())):
+        p = t / float(1 << 16)
+        expect = (halves >= t).astype(np.uint8)
+        np.testing.assert_array_equal(orc.dropout_keep(16, p, seed=0, offset=0)[8:], expect)
+        np.testing.assert_array_equal(orc.dropout_keep(8, p, seed=0, offset=8), expect)

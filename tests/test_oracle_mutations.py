@@ -73,8 +73,13 @@ MUTANTS = [
     ("chan: merge term without / n", "delta * delta * a[0] * b[0] / n", "delta * delta * a[0] * b[0]", 1),
     ("philox: multiplier", "(uint64_t)0xD2511F53u * c0", "(uint64_t)0xD2511F55u * c0", 1),
     ("philox: Weyl key step", "k1 += 0xBB67AE85u;", "k1 += 0x9E3779B9u;", 1),
-    ("mask: word order", "return (w[e & 3] >> 8) >= thresh;", "return (w[3 - (e & 3)] >> 8) >= thresh;", 1),
-    ("mask: counter per element", "const uint64_t blk = e >> 2;", "const uint64_t blk = e;", 1),
+    ("mask: word order", "const uint32_t word = w[(e % 8) / 2];", "const uint32_t word = w[3 - (e % 8) / 2];", 1),
+    ("mask: half order", "(e % 2 == 0) ? (word & 0xFFFFu) : (word >> 16)",
+     "(e % 2 == 1) ? (word & 0xFFFFu) : (word >> 16)", 1),
+    ("mask: four elements per counter", "const uint64_t blk = e / 8;", "const uint64_t blk = e / 4;", 1),
+    ("mask: counter per element", "const uint64_t blk = e / 8;", "const uint64_t blk = e;", 1),
+    ("mask: 24-bit threshold", "return (uint32_t)floor(p * 65536.0 + 0.5);",
+     "return (uint32_t)floor(p * 16777216.0 + 0.5) >> 8;", 1),
     ("mask: seed high word", "(uint32_t)(seed >> 32)}", "0u}", 1),
     ("dropout: survivors not rescaled", "orc_act(act, act_p, x[i]) / (1.0 - p)", "orc_act(act, act_p, x[i])", 1),
     ("dropout: unmasked backward", "dx[i] = orc_kept(offset + (uint64_t)i, seed, t)", "dx[i] = 1", 1),
