@@ -95,8 +95,14 @@ static BnPath choose_path(norm_dtype dt, int64_t C, int64_t HW) {
 // fewer than kBnColMinBlocks workgroups.  Long row bands in about 512
 // workgroups measured faster than more, shorter ones on the BatchNorm1d
 // workloads (8192 x 2048 float32, 2048 x 512 x 32 bf16), and they keep the
-// float64 per-(tile, column) sums small.
-static BnColGeom make_col_geom(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, int V) {
+// float64 per-(tile, column) sums small.  The reduction passes (statistics,
+// backward sums) span 64 vectors of a row per workgroup (one wave's width,
+// 1 KiB); the streaming passes (apply, dx), whose geometry fixes no
+// workspace layout, span 128 (two waves side by side over 2 KiB of each
+// row, two row slices), which measured faster there (bf16 2048 x 512 x 32
+// dx 51.6 -> 47.1 us, float32 8192 x 2048 dx 33.3 -> 32.4 us) but slower for
+// the reductions (their finalize merges twice the tiles).
+static BnColGeom make_col_geom(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, int V, bool stream = false) {
     BnColGeom g;
     const int64_t es = (int64_t)dtype_size(dt);
     g.Nb = Nb;
@@ -118,14 +124,15 @@ static BnColGeom make_col_geom(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW,
     ov_rt = over.first;
     ov_cv = over.second;
 #endif
-    const int64_t cv_max = ov_cv ? ov_cv : kWave;
+    const int64_t cv_cap = stream ? 2 * kWave : kWave;
+    const int64_t cv_max = ov_cv ? ov_cv : cv_cap;
     g.CV = (int)(g.KV < cv_max ? (g.KV > 0 ? g.KV : 1) : cv_max);
     g.RPP = kBnBlock / g.CV;
     g.NCH = (int)ceil_div(g.KV > 0 ? g.KV : 1, g.CV);
     // The row tiling depends on the nominal (vector) width only, so the
     // workspace size does not depend on pointer alignment.
     const int64_t kv_nom = ceil_div(g.K, 16 / es);
-    const int64_t nch_nom = ceil_div(kv_nom > 0 ? kv_nom : 1, kWave);
+    const int64_t nch_nom = ceil_div(kv_nom > 0 ? kv_nom : 1, cv_max);
     int64_t rt = 1024 / es;
     while (rt > 16 && nch_nom * ceil_div(Nb, rt) < kBnColMinBlocks) rt >>= 1;
     if (ov_rt) rt = ov_rt;
@@ -140,9 +147,11 @@ static norm_status check_bn(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW) {
     if (C > (int64_t)1 << 24 || Nb > (int64_t)1 << 31 || HW > (int64_t)1 << 40) return NORM_ERR_SHAPE;
     if (C > 0 && Nb > 0 && HW > 0 && Nb * C > ((int64_t)1 << 31) - 1) return NORM_ERR_SHAPE;
     if (C > 0 && HW > 0 && choose_path(dt, C, HW) == kPathCols) {
-        // Column-path grid: chunks x row tiles must fit one launch.
-        const BnColGeom g = make_col_geom(dt, Nb, C, HW, 1);
-        if ((int64_t)g.NCH * g.T >= ((int64_t)1 << 31)) return NORM_ERR_SHAPE;
+        // Column-path grids: chunks x row tiles must fit one launch.
+        for (bool stream : {false, true}) {
+            const BnColGeom g = make_col_geom(dt, Nb, C, HW, 1, stream);
+            if ((int64_t)g.NCH * g.T >= ((int64_t)1 << 31)) return NORM_ERR_SHAPE;
+        }
     }
     return NORM_OK;
 }
@@ -187,10 +196,11 @@ static norm_status run(norm_dtype dt, int64_t Nb, int64_t C, int64_t HW, BnOp op
             }
         }
         const BnColGeom g = make_col_geom(dt, Nb, C, HW, vec ? VW : 1);
+        const BnColGeom gs = make_col_geom(dt, Nb, C, HW, vec ? VW : 1, true);
         switch (op) {
-        case kOpTrain: return vec ? bn_col_fwd_train<T, VW>(g, a) : bn_col_fwd_train<T, 1>(g, a);
-        case kOpEval: return vec ? bn_col_fwd_eval<T, VW>(g, a) : bn_col_fwd_eval<T, 1>(g, a);
-        default: return vec ? bn_col_bwd<T, VW>(g, a) : bn_col_bwd<T, 1>(g, a);
+        case kOpTrain: return vec ? bn_col_fwd_train<T, VW>(g, gs, a) : bn_col_fwd_train<T, 1>(g, gs, a);
+        case kOpEval: return vec ? bn_col_fwd_eval<T, VW>(gs, a) : bn_col_fwd_eval<T, 1>(gs, a);
+        default: return vec ? bn_col_bwd<T, VW>(g, gs, a) : bn_col_bwd<T, 1>(g, gs, a);
         }
     });
 }

@@ -528,18 +528,21 @@ static auto col_apply_kernel(norm_act act, bool r) {
     }
 }
 
+// g: the reduction geometry (statistics, finalize, workspace layout); gs:
+// the streaming geometry of the apply and dx passes.
 template <typename T, int V>
-norm_status bn_col_fwd_train(const BnColGeom &g, const BnArgs &a) {
+norm_status bn_col_fwd_train(const BnColGeom &g, const BnColGeom &gs, const BnArgs &a) {
     const dim3 grid((unsigned)((int64_t)g.NCH * g.T));
+    const dim3 sgrid((unsigned)((int64_t)gs.NCH * gs.T));
     const dim3 fgrid((unsigned)ceil_div(g.C, kBnWaves));
     double *part = static_cast<double *>(a.ws);
     launch("bn_col_stats_kernel", false, bn_col_stats_kernel<T, V>, grid, dim3(kBnBlock), 0, a.st,
            (const T *)a.x, g, part);
     launch("bn_col_finalize_kernel", false, bn_col_finalize_kernel<T>, fgrid, dim3(kBnBlock), 0, a.st,
            (const double *)part, g, a.eps, a.momentum, a.rm, a.rv, a.sm, a.sr);
-    launch("bn_col_apply_kernel<train>", true, col_apply_kernel<T, V, 0>(a.act, a.res != nullptr), grid,
+    launch("bn_col_apply_kernel<train>", true, col_apply_kernel<T, V, 0>(a.act, a.res != nullptr), sgrid,
            dim3(kBnBlock), 0, a.st, (const T *)a.x, (const T *)a.res, (const T *)a.w, (const T *)a.b,
-           (const float *)a.sm, (const float *)a.sr, a.eps, (T *)a.y, g, (int)a.act, a.act_p);
+           (const float *)a.sm, (const float *)a.sr, a.eps, (T *)a.y, gs, (int)a.act, a.act_p);
     return launch_status();
 }
 
@@ -553,8 +556,9 @@ norm_status bn_col_fwd_eval(const BnColGeom &g, const BnArgs &a) {
 }
 
 template <typename T, int V, int ACT>
-static void col_bwd_act(const BnColGeom &g, const BnArgs &a) {
+static void col_bwd_act(const BnColGeom &g, const BnColGeom &gs, const BnArgs &a) {
     const dim3 grid((unsigned)((int64_t)g.NCH * g.T));
+    const dim3 sgrid((unsigned)((int64_t)gs.NCH * gs.T));
     const dim3 fgrid((unsigned)ceil_div(g.C, kBnWaves));
     const dim3 blk(kBnBlock);
     double *part = static_cast<double *>(a.ws);
@@ -573,18 +577,18 @@ static void col_bwd_act(const BnColGeom &g, const BnArgs &a) {
     if (ACT == kActNone && !has_res) fn = bn_col_bwd_dx_kernel<T, V, ACT, false, 0>;
     else if (has_res && (fp32 || ACT == kActNone)) fn = bn_col_bwd_dx_kernel<T, V, ACT, true, 1>;
     else if (has_res) fn = bn_col_bwd_dx_kernel<T, V, ACT, true, 2>;
-    launch("bn_col_bwd_dx_kernel", !has_res, fn, grid, blk, 0, a.st, (const T *)a.dy, (const T *)a.x,
+    launch("bn_col_bwd_dx_kernel", !has_res, fn, sgrid, blk, 0, a.st, (const T *)a.dy, (const T *)a.x,
            (const T *)a.res, (const T *)a.dres, (const T *)a.w, (const T *)a.b, (const float *)a.sm,
-           (const float *)a.sr, (const float *)coef, (T *)a.dx, g, act_rt, a.act_p);
+           (const float *)a.sr, (const float *)coef, (T *)a.dx, gs, act_rt, a.act_p);
 }
 
 template <typename T, int V>
-norm_status bn_col_bwd(const BnColGeom &g, const BnArgs &a) {
+norm_status bn_col_bwd(const BnColGeom &g, const BnColGeom &gs, const BnArgs &a) {
     switch (a.act) {
-    case NORM_ACT_NONE: col_bwd_act<T, V, kActNone>(g, a); break;
-    case NORM_ACT_RELU: col_bwd_act<T, V, kActRelu>(g, a); break;
-    case NORM_ACT_GELU: col_bwd_act<T, V, kActGelu>(g, a); break;
-    default: col_bwd_act<T, V, kActGeneric>(g, a); break;
+    case NORM_ACT_NONE: col_bwd_act<T, V, kActNone>(g, gs, a); break;
+    case NORM_ACT_RELU: col_bwd_act<T, V, kActRelu>(g, gs, a); break;
+    case NORM_ACT_GELU: col_bwd_act<T, V, kActGelu>(g, gs, a); break;
+    default: col_bwd_act<T, V, kActGeneric>(g, gs, a); break;
     }
     return launch_status();
 }

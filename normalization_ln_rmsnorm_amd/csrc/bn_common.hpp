@@ -214,8 +214,9 @@ struct BnArgs {
 template <typename T, int V> norm_status bn_plane_fwd_train(const BnGeom &g, const BnArgs &a);
 template <typename T, int V> norm_status bn_plane_fwd_eval(const BnGeom &g, const BnArgs &a);
 template <typename T, int V> norm_status bn_plane_bwd(const BnGeom &g, const BnArgs &a);
-template <typename T, int V> norm_status bn_col_fwd_train(const BnColGeom &g, const BnArgs &a);
-template <typename T, int V> norm_status bn_col_fwd_eval(const BnColGeom &g, const BnArgs &a);
-template <typename T, int V> norm_status bn_col_bwd(const BnColGeom &g, const BnArgs &a);
+// Column path: g the reduction geometry, gs the streaming one (apply, dx).
+template <typename T, int V> norm_status bn_col_fwd_train(const BnColGeom &g, const BnColGeom &gs, const BnArgs &a);
+template <typename T, int V> norm_status bn_col_fwd_eval(const BnColGeom &gs, const BnArgs &a);
+template <typename T, int V> norm_status bn_col_bwd(const BnColGeom &g, const BnColGeom &gs, const BnArgs &a);
 
 }  // namespace mi355norm

@@ -23,9 +23,9 @@ constexpr int kVW = 16 / (int)sizeof(IoT);
     template norm_status bn_plane_fwd_train<IoT, V>(const BnGeom &, const BnArgs &); \
     template norm_status bn_plane_fwd_eval<IoT, V>(const BnGeom &, const BnArgs &);  \
     template norm_status bn_plane_bwd<IoT, V>(const BnGeom &, const BnArgs &);       \
-    template norm_status bn_col_fwd_train<IoT, V>(const BnColGeom &, const BnArgs &); \
+    template norm_status bn_col_fwd_train<IoT, V>(const BnColGeom &, const BnColGeom &, const BnArgs &); \
     template norm_status bn_col_fwd_eval<IoT, V>(const BnColGeom &, const BnArgs &); \
-    template norm_status bn_col_bwd<IoT, V>(const BnColGeom &, const BnArgs &);
+    template norm_status bn_col_bwd<IoT, V>(const BnColGeom &, const BnColGeom &, const BnArgs &);
 
 MI355NORM_INST(kVW)
 MI355NORM_INST(1)
