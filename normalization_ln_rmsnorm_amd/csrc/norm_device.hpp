@@ -313,9 +313,10 @@ __device__ __forceinline__ unsigned xcd_swizzle(unsigned b, unsigned G) {
 //    u = |z| / sqrt 2 the exp(-u^2) is exp(-z^2 / 2), the same factor phi
 //    needs, so Phi and phi share one exp; in float32 the result is within
 //    3e-7 of Phi (and of GELU') everywhere -- far inside 2 bf16 ulp.
-//    The coefficients below are A&S's a1..a5 halved (they give Phi(-|z|)
-//    = erfc(u) / 2 directly).  This form serves the derivative, which needs
-//    both Phi and phi; the forward uses the cheaper gelu_fast below.
+//    Divided by the sqrt(2 pi) / 2 that relates exp(-u^2) / 2 to phi, the
+//    coefficients are A&S eq. 26.2.17's b1..b5 (Phi(-|z|) = phi(z) t B(t),
+//    |error| < 7.5e-8).  This form serves the derivative, which needs both
+//    Phi and phi; the forward uses the cheaper gelu_fast below.
 enum Act : int {
     kActNone = 0, kActRelu = 1, kActGelu = 2, kActSigmoid = 3, kActTanh = 4, kActSilu = 5,
     kActMish = 6, kActLeakyRelu = 7, kActElu = 8, kActSelu = 9, kActCelu = 10,
@@ -333,42 +334,49 @@ __device__ __forceinline__ float gelu_grad_exact(float z) {
     return fmaf(z * kInvSqrt2Pi, expf(-0.5f * z * z), 0.5f * (1.0f + erff(z * kInvSqrt2)));
 }
 
-// Fast GELU'(z) (FAST = true).  With e = exp(-z^2 / 2) and Phi(-|z|) =
-// P(t) t e (the halved 7.1.26 polynomial P, t = 1 / (1 + p |z| / sqrt 2)):
-// Phi(z) = H(z) - s P(t) t e with s = sign(z) and H = (1 + s) / 2 (1 for
-// z >= 0, 0 below), so GELU'(z) = H + e (z / sqrt(2 pi) - P(t) s t).  The
-// sign rides in the reciprocal: s t = 1 / (s + p z / sqrt 2) (both terms
-// carry the sign of z), and P takes |s t| = t through the operand's
-// absolute-value modifier; s itself is one bit-select (copysign), H one
-// FMA.  That replaces the compare and the two selects of the plain form.
+// Fast GELU'(z) (FAST = true).  With phi(z) = exp(-z^2 / 2) / sqrt(2 pi)
+// and Phi(-|z|) = phi(z) t B(t) (B the 7.1.26 polynomial divided by
+// sqrt(2 pi) / 2, i.e. the b1..b5 of A&S eq. 26.2.17; t = 1 / (1 + p |z|),
+// p = 0.2316419): Phi(z) = H(z) - s phi(z) t B(t) with s = sign(z) and
+// H = (1 + s) / 2 (1 for z >= 0, 0 below), so GELU'(z) = H + phi(z) (z -
+// B(t) s t).  phi(z) is one exp2 whose argument carries log2(1 / sqrt(2 pi))
+// (so z needs no scaling multiply).  The sign rides in the reciprocal:
+// s t = 1 / (s + p z) (both terms carry the sign of z), and B takes
+// |s t| = t through the operand's absolute-value modifier; s itself is one
+// bit-select (copysign), H one FMA.  That replaces the compare and the two
+// selects of the plain form.
+constexpr float kLog2InvSqrt2Pi = -1.32574806f;  // log2(1 / sqrt(2 pi))
 __device__ __forceinline__ float sign_of(float v) { return __builtin_copysignf(1.0f, v); }
 __device__ __forceinline__ float gelu_grad_fast(float z) {
-    const float e = __builtin_amdgcn_exp2f(z * z * kNegHalfLog2e);
+    const float e = __builtin_amdgcn_exp2f(fmaf(z * z, kNegHalfLog2e, kLog2InvSqrt2Pi));  // phi(z)
     const float sg = sign_of(z);
-    const float st = __builtin_amdgcn_rcpf(fmaf(0.3275911f * kInvSqrt2, z, sg));  // s t
+    const float st = __builtin_amdgcn_rcpf(fmaf(0.2316419f, z, sg));  // s t
     const float t = fabsf(st);
-    float p = fmaf(t, 0.5307027145f, -0.7265760135f);
-    p = fmaf(t, p, 0.7107068705f);
-    p = fmaf(t, p, -0.142248368f);
-    p = fmaf(t, p, 0.127414796f);
-    return fmaf(e, fmaf(-p, st, z * kInvSqrt2Pi), fmaf(0.5f, sg, 0.5f));
+    float b = fmaf(t, 1.330274429f, -1.821255978f);
+    b = fmaf(t, b, 1.781477937f);
+    b = fmaf(t, b, -0.356563782f);
+    b = fmaf(t, b, 0.319381530f);
+    return fmaf(e, fmaf(-b, st, z), fmaf(0.5f, sg, 0.5f));
 }
 
 // gelu_grad_fast of z = w / kGeluWScale.  A caller that forms z as x a + s
 // can scale a and s by kGeluWScale = sqrt(log2(e) / 2) once and pass w: the
-// exp2 argument -z^2 log2(e) / 2 is then -w^2, one multiply per element
-// fewer; the other constants absorb 1 / kGeluWScale.  Same error bound.
+// exp2 argument -z^2 log2(e) / 2 is then -w^2 (one multiply per element
+// fewer), phi(z) = exp2(log2(1 / sqrt(2 pi)) - w^2), and GELU'(z) = H +
+// (phi / kGeluWScale) (w - kGeluWScale B(t) s t): the factor 1 /
+// kGeluWScale joins the exponent (log2 of 1 / (sqrt(2 pi) kGeluWScale)),
+// kGeluWScale joins B's coefficients and p.  Same error bound.
 constexpr float kGeluWScale = 0.84932180f;
 __device__ __forceinline__ float gelu_grad_fast_w(float w) {
-    const float e = __builtin_amdgcn_exp2f(-w * w);
+    const float e = __builtin_amdgcn_exp2f(fmaf(-w, w, -1.09013125f));  // phi / kGeluWScale
     const float sg = sign_of(w);
-    const float st = __builtin_amdgcn_rcpf(fmaf(0.27273747f, w, sg));  // p / sqrt 2 / kGeluWScale
+    const float st = __builtin_amdgcn_rcpf(fmaf(0.27273747f, w, sg));  // p / kGeluWScale
     const float t = fabsf(st);
-    float p = fmaf(t, 0.5307027145f, -0.7265760135f);
-    p = fmaf(t, p, 0.7107068705f);
-    p = fmaf(t, p, -0.142248368f);
-    p = fmaf(t, p, 0.127414796f);
-    return fmaf(e, fmaf(-p, st, w * 0.46971864f), fmaf(0.5f, sg, 0.5f));  // 1 / sqrt(2 pi) / kGeluWScale
+    float b = fmaf(t, 1.129831073f, -1.546832407f);  // kGeluWScale b5, b4
+    b = fmaf(t, b, 1.513048048f);
+    b = fmaf(t, b, -0.3028373926f);
+    b = fmaf(t, b, 0.2712576963f);
+    return fmaf(e, fmaf(-b, st, w), fmaf(0.5f, sg, 0.5f));
 }
 
 // Fast forward GELU (FAST = true).  The forward needs Phi but not phi, so it
