@@ -57,3 +57,44 @@ def test_shape_beyond_the_scratch_is_refused():
         nl.rms_bwd_noalloc(x, x, None, rstd, dx=dx, dw=dw)
     torch.cuda.synchronize()
     assert bool((dx == 7.0).all()) and bool((dw == 7.0).all())
+
+
+def test_graph_capture_replays():
+    """The callers this entry point is for include stream capture: an RMSNorm
+    forward + no-allocation backward recorded in a graph, replayed three
+    times with eager work in between (a no-allocation backward of another
+    shape, which overwrites the scratch), reproduces the eager outputs bit
+    for bit on every replay."""
+    print("case noalloc graph capture 2000x2048", flush=True)
+    gen = torch.Generator().manual_seed(7)
+    bf = torch.bfloat16
+    x = torch.randn(2000, 2048, generator=gen).to(bf).cuda()
+    dy = torch.randn(2000, 2048, generator=gen).to(bf).cuda()
+    w = (1.0 + 0.05 * torch.randn(2048, generator=gen)).to(bf).cuda()
+    y, rstd = torch.empty_like(x), torch.empty(2000, device="cuda")
+    dx, dw = torch.empty_like(x), torch.empty(2048, dtype=bf, device="cuda")
+
+    def step():
+        nl.rms_fwd(x, w, 1e-6, y=y, rstd=rstd)
+        nl.rms_bwd_noalloc(dy, x, w, rstd, dx=dx, dw=dw)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (y, rstd, dx, dw)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    xo = torch.randn(700, 512, generator=gen).to(bf).cuda()
+    wo = torch.ones(512, dtype=bf, device="cuda")
+    dxo, dwo = torch.empty_like(xo), torch.empty_like(wo)
+    for replay in range(3):
+        for t in (y, rstd, dx, dw):
+            t.fill_(float("nan"))
+        _, ro = nl.rms_fwd(xo, wo, 1e-6)
+        nl.rms_bwd_noalloc(xo, xo, wo, ro, dx=dxo, dw=dwo)  # eager use of the same scratch
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t, r in zip(("y", "rstd", "dx", "dw"), (y, rstd, dx, dw), ref):
+            assert torch.equal(t.view(torch.uint8), r.view(torch.uint8)), f"replay {replay}: {name}"
