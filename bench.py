@@ -517,8 +517,8 @@ def cpu_baseline(bench, budget_s):
     return {"value": step_bytes / per_step / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{wl.name}: {calls} oracle call(s) on groups of {group} of its {units} "
-                      f"{unit_name} ({done} {unit_name} = {frac:.3g} of the workload's step: "
-                      f"{', '.join(bench.ops)}), {spent:.1f} s; float64 C oracle, OpenMP; inputs "
+                      f"{unit_name} ({done} {unit_name} processed = {frac:.3g} times the workload's "
+                      f"step of {', '.join(bench.ops)}), {spent:.1f} s; float64 C oracle, OpenMP; inputs "
                       f"widened to float64 outside the timing",
             "s_per_step": per_step, "rows_per_s": wl.rows / per_step, "cpu_model": model}
 
