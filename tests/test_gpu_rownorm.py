@@ -214,6 +214,17 @@ def test_empty_batch_is_noop(orc):
 
 
 @pytest.mark.parametrize("kind", ["ln", "rms"])
+@pytest.mark.parametrize("dtype,M,N", [("f32", 5000003, 4), ("bf16", 5000003, 8)])
+def test_persistent_forward_grid(orc, kind, dtype, M, N):
+    """Narrow rows in so many row groups that the forward grid is capped and
+    each block loops over several groups with the next one's loads issued
+    ahead (the other shapes here give every block one group); a row count
+    that leaves the last group partly filled."""
+    print(f"case {kind} {dtype} {M}x{N} (persistent forward)", flush=True)
+    run_case(orc, kind, dtype, M, N)
+
+
+@pytest.mark.parametrize("kind", ["ln", "rms"])
 def test_rows_past_2_32_elements(orc, kind):
     """bf16, 63 x 16646 = 1048698 rows x 4096 (past 2^32 elements, 8 GiB per
     tensor): every element index of the row path beyond 32 bits.  Rows are
