@@ -34,7 +34,13 @@
 namespace mi355norm {
 
 constexpr int kAdBlock = 256;
-constexpr int kAdUnroll = 4;  // vectors per thread
+// Vectors per thread and pass, as measured on the bf16 GELU 16384 x 4096
+// workload: the forward (VALU-heavy with the generator) runs best with one
+// (48.5 -> 46.9 us against four), the backward with two (63.7 -> 58.5 us):
+// more threads in flight, each with fewer loads, hide the per-element
+// arithmetic better than more loads per thread.
+constexpr int kAdUnrollFwd = 1;
+constexpr int kAdUnrollBwd = 2;
 
 struct AdArgs {
     int64_t n;           // elements
@@ -105,7 +111,7 @@ __device__ __forceinline__ void keep_flags(const AdArgs &a, int64_t vi, bool kee
     }
 }
 
-// Forward over vectors v0, v0 + stride, ... below nvec, kAdUnroll loads in
+// Forward over vectors v0, v0 + stride, ... below nvec, kAdUnrollFwd loads in
 // flight (vector v holds elements v * V .. v * V + V - 1).  DROP = false is
 // the plain activation (p = 0: no generator calls).  `ub` is a vector index
 // at or below v0 that is the same in every lane (the range's first vector);
@@ -115,15 +121,15 @@ __device__ __forceinline__ void ad_fwd_range(const T *__restrict__ x, T *__restr
                                              int64_t v0, int64_t stride, int64_t ub, const AdArgs &a) {
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
-    for (int64_t vb = v0; vb < nvec; vb += stride * kAdUnroll) {
-        raw_t r[kAdUnroll];
+    for (int64_t vb = v0; vb < nvec; vb += stride * kAdUnrollFwd) {
+        raw_t r[kAdUnrollFwd];
 #pragma unroll
-        for (int u = 0; u < kAdUnroll; ++u) {
+        for (int u = 0; u < kAdUnrollFwd; ++u) {
             const int64_t v = vb + u * stride;
             if (v < nvec) r[u] = vload_stream<T, V>(x + v * V);
         }
 #pragma unroll
-        for (int u = 0; u < kAdUnroll; ++u) {
+        for (int u = 0; u < kAdUnrollFwd; ++u) {
             const int64_t v = vb + u * stride;
             if (v < nvec) {
                 float f[V], o[V];
@@ -148,10 +154,10 @@ __device__ __forceinline__ void ad_bwd_range(const T *__restrict__ dy, const T *
     using VT = Vec<T, V>;
     using raw_t = typename VT::raw_t;
     constexpr bool kFast = sizeof(T) == 2;
-    for (int64_t vb = v0; vb < nvec; vb += stride * kAdUnroll) {
-        raw_t rd[kAdUnroll], rx[kAdUnroll];
+    for (int64_t vb = v0; vb < nvec; vb += stride * kAdUnrollBwd) {
+        raw_t rd[kAdUnrollBwd], rx[kAdUnrollBwd];
 #pragma unroll
-        for (int u = 0; u < kAdUnroll; ++u) {
+        for (int u = 0; u < kAdUnrollBwd; ++u) {
             const int64_t v = vb + u * stride;
             if (v < nvec) {
                 rd[u] = vload_stream<T, V>(dy + v * V);
@@ -159,7 +165,7 @@ __device__ __forceinline__ void ad_bwd_range(const T *__restrict__ dy, const T *
             }
         }
 #pragma unroll
-        for (int u = 0; u < kAdUnroll; ++u) {
+        for (int u = 0; u < kAdUnrollBwd; ++u) {
             const int64_t v = vb + u * stride;
             if (v < nvec) {
                 float df[V], xf[V], o[V];
@@ -184,11 +190,11 @@ template <typename T, int V, int ACT, bool DROP>
 __global__ void __launch_bounds__(kAdBlock)
 act_dropout_fwd_kernel(const T *__restrict__ x, T *__restrict__ y, AdArgs a) {
     const int64_t nvec = a.n / V;
-    const int64_t t0 = (int64_t)blockIdx.x * kAdBlock * kAdUnroll + threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * kAdBlock * kAdUnroll;
-    // Each block covers kAdUnroll * kAdBlock consecutive vectors per pass.
-    for (int64_t base = (int64_t)blockIdx.x * kAdBlock * kAdUnroll; base < nvec; base += stride)
-        ad_fwd_range<T, V, ACT, DROP>(x, y, base + kAdBlock * kAdUnroll < nvec ? base + kAdBlock * kAdUnroll : nvec,
+    const int64_t t0 = (int64_t)blockIdx.x * kAdBlock * kAdUnrollFwd + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kAdBlock * kAdUnrollFwd;
+    // Each block covers kAdUnrollFwd * kAdBlock consecutive vectors per pass.
+    for (int64_t base = (int64_t)blockIdx.x * kAdBlock * kAdUnrollFwd; base < nvec; base += stride)
+        ad_fwd_range<T, V, ACT, DROP>(x, y, base + kAdBlock * kAdUnrollFwd < nvec ? base + kAdBlock * kAdUnrollFwd : nvec,
                                       base + threadIdx.x, kAdBlock, base, a);
     if (V > 1) {
         const int64_t tail = a.n - nvec * V;
@@ -203,10 +209,10 @@ template <typename T, int V, int ACT, bool DROP>
 __global__ void __launch_bounds__(kAdBlock)
 act_dropout_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, T *__restrict__ dx, AdArgs a) {
     const int64_t nvec = a.n / V;
-    const int64_t t0 = (int64_t)blockIdx.x * kAdBlock * kAdUnroll + threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * kAdBlock * kAdUnroll;
-    for (int64_t base = (int64_t)blockIdx.x * kAdBlock * kAdUnroll; base < nvec; base += stride)
-        ad_bwd_range<T, V, ACT, DROP>(dy, x, dx, base + kAdBlock * kAdUnroll < nvec ? base + kAdBlock * kAdUnroll : nvec,
+    const int64_t t0 = (int64_t)blockIdx.x * kAdBlock * kAdUnrollBwd + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * kAdBlock * kAdUnrollBwd;
+    for (int64_t base = (int64_t)blockIdx.x * kAdBlock * kAdUnrollBwd; base < nvec; base += stride)
+        ad_bwd_range<T, V, ACT, DROP>(dy, x, dx, base + kAdBlock * kAdUnrollBwd < nvec ? base + kAdBlock * kAdUnrollBwd : nvec,
                                       base + threadIdx.x, kAdBlock, base, a);
     if (V > 1) {
         const int64_t tail = a.n - nvec * V;
