@@ -315,7 +315,8 @@ def bn_bwd(dy, x, w, b, save_mean, save_rstd, act="none", res=None, *, act_param
 # ------------------------------------------------------ activation + dropout
 def act_dropout_fwd(x, act="none", drop_p=0.0, seed=0, offset=0, *, act_param=0.0, y=None):
     """y = act(x) with inverted dropout (probability drop_p), element-wise;
-    the mask is a function of (seed, offset + element index)."""
+    the mask is a function of (seed, offset + element index).  offset must
+    be a multiple of 8 (one generator call serves eight elements)."""
     y = torch.empty_like(x) if y is None else y
     _same(y, x, "y")
     if y.numel() != x.numel():
