@@ -29,10 +29,13 @@
  *   once, at the store (fp16 results beyond its range become +-inf).
  * Streams.  `stream` is a hipStream_t (NULL = the legacy default stream).
  *   Kernels are enqueued on it and the call returns without synchronizing.
+ *   Launch geometry is planned from the current device's compute-unit
+ *   count, so the stream should belong to the current device.
  * Ownership.  The caller allocates and owns every buffer, including the
  *   workspace; the library never allocates, frees or synchronizes, and keeps
  *   no state between calls (apart from the process-wide test hook
- *   norm_bn_force_path and the per-thread timing hook below).  Concurrent
+ *   norm_bn_force_path, the per-thread timing hook below and the static
+ *   per-GPU scratch of rms_bwd_noalloc).  Concurrent
  *   calls are safe if they use distinct output and workspace buffers.
  *   Outputs must not alias inputs.
  * Capture.  A call enqueues kernels only (no memset, copy or host wait), so
@@ -169,7 +172,8 @@ norm_status rms_bwd(norm_dtype dt, int64_t M, int64_t N, const void *dy,
  * must be serialized by the caller.  Nothing in the array needs to start at
  * zero (every partial row is written before it is read); it keeps the last
  * call's contents.  NORM_ERR_HIP if the runtime cannot resolve the array's
- * address on the current device.                                          */
+ * address on the stream's device (the current device for the null
+ * stream).                                                                */
 #define NORM_NOALLOC_SCRATCH_BYTES (16u << 20)
 norm_status rms_bwd_noalloc(norm_dtype dt, int64_t M, int64_t N, const void *dy,
                             const void *x, const void *w, const float *rstd,

@@ -182,17 +182,32 @@ std::atomic<void *> g_scratch_ptr[kScratchDevices];
 std::mutex g_scratch_mutex;
 }  // namespace
 
-// The current device's address of `scratch` (nullptr if the runtime fails).
-static void *static_scratch() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+// The address of `scratch` on the device the stream `s` belongs to (the
+// current device for the null stream); nullptr if the runtime fails.  The
+// first use on a device takes the address with that device current and
+// restores the caller's current device afterwards.
+static void *static_scratch(hipStream_t s) {
+    int dev = -1;
+    if (s) {
+        hipDevice_t d;
+        if (hipStreamGetDevice(s, &d) != hipSuccess) return nullptr;
+        dev = (int)d;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kScratchDevices) return nullptr;
     void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
     if (p) return p;
     std::lock_guard<std::mutex> lock(g_scratch_mutex);
     p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
     if (!p) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
         void *addr = nullptr;
-        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+        const bool ok = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) == hipSuccess && addr;
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return nullptr;
+        if (!ok) return nullptr;
         g_scratch_ptr[dev].store(addr, std::memory_order_release);
         p = addr;
     }
@@ -256,7 +271,7 @@ static norm_status bwd_entry(norm_dtype dt, int64_t M, int64_t N, const void *dy
         const size_t used = (want && !direct) ? part_stride * sizeof(float) * (RMS ? 1 : 2) : 0;
         if (used > kScratchBytes) return NORM_ERR_WORKSPACE;
         if (used) {
-            ws = static_scratch();
+            ws = static_scratch(s);
             if (!ws) return NORM_ERR_HIP;
         }
     }
