@@ -18,9 +18,9 @@
 // are scaled by 1 / (1 - p).
 //
 // Both directions are bound by HBM traffic (2 tensors forward, 3 backward);
-// the ten Philox rounds are 20 64-bit multiplies and 40 XORs per call, so
-// taking 16 bits per element (one call per 16-bit vector, not two) is what
-// keeps the 16-bit GELU forward near the HBM rate.
+// the ten Philox rounds are 20 64-bit multiplies and 20 three-input XORs
+// per call, so taking 16 bits per element (one call per 16-bit vector, not
+// two) is what keeps the 16-bit GELU forward near the HBM rate.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -52,6 +52,12 @@ struct AdArgs {
     float act_p;         // its parameter
 };
 
+// a ^ b ^ c as one v_bitop3_b32: 0x96 is the truth table of the three
+// inputs' parity (the compiler leaves a chain of two-input XORs unfused).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 // Philox4x32-10 on counter (c0, c1, 0, 0): ten rounds of the published
 // round function, the key bumped by the Weyl constants between rounds.
 __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1,
@@ -65,8 +71,8 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
         const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
         const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
         const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
-        const uint32_t n0 = hi1 ^ c1 ^ k0;
-        const uint32_t n2 = hi0 ^ c3 ^ k1;
+        const uint32_t n0 = xor3(hi1, c1, k0);
+        const uint32_t n2 = xor3(hi0, c3, k1);
         c0 = n0;
         c1 = lo1;
         c2 = n2;

@@ -389,6 +389,15 @@ __device__ __forceinline__ float gelu_grad_fast_w(float w) {
 // reciprocal's 16th power is r16 / 2 and the result one FMA.  In float32
 // the result is within 7.1e-7 of GELU(z) (below 0.04 bf16 ulp wherever
 // |GELU(z)| > 2^-10).
+// max(z, 0) as one integer max on the bits: a float with the sign bit set is
+// a negative int32 and gives +0, any other float passes unchanged.  fmaxf
+// costs a second v_max_f32 that quiets signalling NaNs of a value that came
+// straight from memory.  Used where it is added to a term that carries z's
+// NaN or infinity anyway, and where the sign of a zero result is immaterial.
+__device__ __forceinline__ float max0_bits(float z) {
+    return __int_as_float(max(__float_as_int(z), 0));
+}
+
 __device__ __forceinline__ float gelu_fast(float z) {
     const float az = fabsf(z);
     float p = fmaf(5.6212998e-06f, az, 5.1055209e-05f);
@@ -402,7 +411,7 @@ __device__ __forceinline__ float gelu_fast(float z) {
     r *= r;
     r *= r;
     r *= r;  // r = p^-16 = r16 / 2
-    return fmaf(-az, r, fmaxf(z, 0.0f));
+    return fmaf(-az, r, max0_bits(z));
 }
 
 // GELU with a small relative error everywhere, the forward for fp16 I/O:
@@ -428,7 +437,7 @@ __device__ __forceinline__ float gelu_fast_rel(float z) {
     p = fmaf(t, p, 1.442729235e+00f);
     const float arg = fmaf(t, p, fmaf(z, z * -7.213475108e-01f, -2.825748205e+00f));
     const float h = t * __builtin_amdgcn_exp2f(arg);  // erfc(u) / 2
-    return fmaf(-az, h, fmaxf(z, 0.0f));
+    return fmaf(-az, h, max0_bits(z));
 }
 
 template <int ACT, bool FAST = false> __device__ __forceinline__ float act_fwd(float z) {
