@@ -482,8 +482,9 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
             const int64_t off = (int64_t)blockIdx.x * N + (int64_t)v * V;
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                if (part_w) part_w[off + e] = acc_w[k][e];
-                if (part_b) part_b[off + e] = acc_b[k][e];
+                const uint32_t c = (uint32_t)(v * V + e);
+                if (part_w) vstore_out<float, 1>(part_w + (int64_t)blockIdx.x * N, c, __float_as_uint(acc_w[k][e]));
+                if (part_b) vstore_out<float, 1>(part_b + (int64_t)blockIdx.x * N, c, __float_as_uint(acc_b[k][e]));
                 if (dw_out) st1(dw_out + (off + e), acc_w[k][e]);
                 if (db_out) st1(db_out + (off + e), acc_b[k][e]);
             }
@@ -509,13 +510,32 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
             }
         }
         __syncthreads();
+        if (out == nullptr && (N & 3) == 0) {
+            // Four columns per thread: 16-byte LDS reads and one 16-byte
+            // device-scope store (as for dx) per four columns, so the partial
+            // rows leave no dirty L2 lines for the write-back at the end of
+            // the kernel.  Each column's slots are added in the same order.
+            float *prow = part + (int64_t)blockIdx.x * N;
+            for (int col = threadIdx.x * 4; col < N; col += blockDim.x * 4) {
+                float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int r = 0; r < rpb; ++r) {
+                    const float4 q = *reinterpret_cast<const float4 *>(colbuf + r * N + col);
+                    sum[0] += q.x;
+                    sum[1] += q.y;
+                    sum[2] += q.z;
+                    sum[3] += q.w;
+                }
+                vstore_out<float, 4>(prow, (uint32_t)col, Vec<float, 4>::pack(sum));
+            }
+            continue;
+        }
         for (int col = threadIdx.x; col < N; col += blockDim.x) {
             float sum = 0.0f;
             for (int r = 0; r < rpb; ++r) sum += colbuf[r * N + col];
             if (out)
                 st1(out + col, sum);
             else
-                part[(int64_t)blockIdx.x * N + col] = sum;
+                vstore_out<float, 1>(part + (int64_t)blockIdx.x * N, (uint32_t)col, __float_as_uint(sum));
         }
     }
 }
