@@ -494,7 +494,7 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
     // Several row slots: stage every slot's column partials in LDS as
     // [slot][column], then let all threads add over the slots (in slot
     // order) for their own columns and write the block's partial row.
-    extern __shared__ float colbuf[];  // rpb * N floats
+    extern __shared__ __align__(16) float colbuf[];  // rpb * N floats; 16-byte reads below
     for (int which = 0; which < 2; ++which) {
         float *part = which == 0 ? part_w : part_b;
         T *out = which == 0 ? dw_out : db_out;
