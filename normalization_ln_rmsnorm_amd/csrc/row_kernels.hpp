@@ -504,9 +504,17 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
         for (int k = 0; k < IT; ++k) {
             const int v = lane + k * tpr;
             if (v < nv) {
+                float *dst = colbuf + slot_in_block * N + v * V;
+                if constexpr (V % 4 == 0) {  // N is a multiple of V here: 16-byte writes
 #pragma unroll
-                for (int e = 0; e < V; ++e)
-                    colbuf[slot_in_block * N + v * V + e] = which == 0 ? acc_w[k][e] : acc_b[k][e];
+                    for (int e = 0; e < V; e += 4) {
+                        const float *a = which == 0 ? &acc_w[k][e] : &acc_b[k][e];
+                        *reinterpret_cast<float4 *>(dst + e) = make_float4(a[0], a[1], a[2], a[3]);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < V; ++e) dst[e] = which == 0 ? acc_w[k][e] : acc_b[k][e];
+                }
             }
         }
         __syncthreads();
