@@ -492,19 +492,18 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
         return;
     }
     // Several row slots: stage every slot's column partials in LDS as
-    // [slot][column], then let all threads add over the slots (in slot
-    // order) for their own columns and write the block's partial row.
-    extern __shared__ __align__(16) float colbuf[];  // rpb * N floats; 16-byte reads below
-    for (int which = 0; which < 2; ++which) {
-        float *part = which == 0 ? part_w : part_b;
-        T *out = which == 0 ? dw_out : db_out;
-        if (part == nullptr && out == nullptr) continue;
-        __syncthreads();
+    // [which][slot][column] (dW, then dB when wanted: one staging between
+    // two barriers), then let all threads add over the slots (in slot order)
+    // for their own columns and write the block's partial rows.
+    extern __shared__ __align__(16) float colbuf[];  // (1 or 2) * rpb * N floats; 16-byte access below
+    const bool want_b = part_b != nullptr || db_out != nullptr;
+    __syncthreads();
+    for (int which = 0; which < (want_b ? 2 : 1); ++which) {
 #pragma unroll
         for (int k = 0; k < IT; ++k) {
             const int v = lane + k * tpr;
             if (v < nv) {
-                float *dst = colbuf + slot_in_block * N + v * V;
+                float *dst = colbuf + (which * rpb + slot_in_block) * N + v * V;
                 if constexpr (V % 4 == 0) {  // N is a multiple of V here: 16-byte writes
 #pragma unroll
                     for (int e = 0; e < V; e += 4) {
@@ -517,7 +516,13 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
                 }
             }
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    for (int which = 0; which < 2; ++which) {
+        float *part = which == 0 ? part_w : part_b;
+        T *out = which == 0 ? dw_out : db_out;
+        if (part == nullptr && out == nullptr) continue;
+        const float *src = colbuf + which * rpb * N;
         if (out == nullptr && (N & 3) == 0) {
             // Four columns per thread: 16-byte LDS reads and one 16-byte
             // device-scope store (as for dx) per four columns, so the partial
@@ -527,7 +532,7 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
             for (int col = threadIdx.x * 4; col < N; col += blockDim.x * 4) {
                 float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
                 for (int r = 0; r < rpb; ++r) {
-                    const float4 q = *reinterpret_cast<const float4 *>(colbuf + r * N + col);
+                    const float4 q = *reinterpret_cast<const float4 *>(src + r * N + col);
                     sum[0] += q.x;
                     sum[1] += q.y;
                     sum[2] += q.z;
@@ -539,7 +544,7 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
         }
         for (int col = threadIdx.x; col < N; col += blockDim.x) {
             float sum = 0.0f;
-            for (int r = 0; r < rpb; ++r) sum += colbuf[r * N + col];
+            for (int r = 0; r < rpb; ++r) sum += src[r * N + col];
             if (out)
                 st1(out + col, sum);
             else
@@ -643,7 +648,8 @@ norm_status row_launch_bwd(const RowPlan &p, hipStream_t s, const void *dy, cons
     if (!fn) return NORM_ERR_SHAPE;
     const int rpb = p.block / p.tpr;
     const bool sums = part_w || part_b || dw_out || db_out;
-    const size_t shmem = (sums && rpb > 1) ? (size_t)rpb * N * sizeof(float) : 0;
+    const size_t nstage = (part_b || db_out) ? 2 : 1;  // dW, and dB when wanted
+    const size_t shmem = (sums && rpb > 1) ? nstage * rpb * N * sizeof(float) : 0;
     if (shmem > 65536) return NORM_ERR_SHAPE;  // only reachable through the tuning override
     launch(RMS ? "row_bwd_kernel<rms>" : "row_bwd_kernel<ln>", true, fn, dim3(p.grid), dim3(p.block), shmem, s,
            (const T *)dy, (const T *)x, (const T *)w, mean, rstd, (T *)dx, part_w, part_b, (T *)dw_out,
