@@ -480,11 +480,23 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
             const int v = lane + k * tpr;
             if (v >= nv) continue;
             const int64_t off = (int64_t)blockIdx.x * N + (int64_t)v * V;
+            if constexpr (V % 4 == 0) {  // N is a multiple of V here: 16-byte stores
+#pragma unroll
+                for (int e = 0; e < V; e += 4) {
+                    const uint32_t c = (uint32_t)(v * V + e);
+                    if (part_w) vstore_out<float, 4>(part_w + (int64_t)blockIdx.x * N, c, Vec<float, 4>::pack(&acc_w[k][e]));
+                    if (part_b) vstore_out<float, 4>(part_b + (int64_t)blockIdx.x * N, c, Vec<float, 4>::pack(&acc_b[k][e]));
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const uint32_t c = (uint32_t)(v * V + e);
+                    if (part_w) vstore_out<float, 1>(part_w + (int64_t)blockIdx.x * N, c, __float_as_uint(acc_w[k][e]));
+                    if (part_b) vstore_out<float, 1>(part_b + (int64_t)blockIdx.x * N, c, __float_as_uint(acc_b[k][e]));
+                }
+            }
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                const uint32_t c = (uint32_t)(v * V + e);
-                if (part_w) vstore_out<float, 1>(part_w + (int64_t)blockIdx.x * N, c, __float_as_uint(acc_w[k][e]));
-                if (part_b) vstore_out<float, 1>(part_b + (int64_t)blockIdx.x * N, c, __float_as_uint(acc_b[k][e]));
                 if (dw_out) st1(dw_out + (off + e), acc_w[k][e]);
                 if (db_out) st1(db_out + (off + e), acc_b[k][e]);
             }
