@@ -258,6 +258,28 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
     using raw_t = typename VT::raw_t;
     int c; int64_t n0, n1;
     tile_of_block(g, &c, &n0, &n1);
+    const int64_t nvp = g.HW / V;
+    // Vectors in flight per thread: 8, or 4 for the 16-bit training apply
+    // (bf16 GELU BatchNorm2d 256x64x112x112: 125.7 -> 123.0 us; the float32
+    // apply measured flat at 4, the eval apply keeps 8).
+    constexpr int U = (sizeof(T) == 2 && MODE == 0) ? 4 : kBnUnrollStream;
+    raw_t rx[U], rr[U];
+    auto load = [&](int64_t off, int64_t v0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + (int64_t)u * kBnBlock;
+            if (v < nvp) {
+                rx[u] = vload_stream<T, V>(x + off + v * V);
+                if (RES) rr[u] = vload_stream<T, V>(res + off + v * V);
+            }
+        }
+    };
+    // Float32 I/O: the block's first vectors are requested before the
+    // channel's statistics are formed, so that read overlaps them (apply
+    // 89.4 -> 87.9 us on the float32 BatchNorm2d workload; the 16-bit
+    // kernels measured slower with it: eval apply 120.7 -> 127.2 us).
+    bool loaded = sizeof(T) == 4 && n0 < n1;
+    if (loaded) load(plane_offset(g, n0, c), threadIdx.x);
     float mean, rstd;
     if (MODE == 0) {
         const WelfD st = merge_channel_tiles(part, c, g.tiles);
@@ -272,25 +294,13 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
     float a, s;
     const float bias = b ? ld1(b + c) : 0.0f;
     bn_coeffs(mean, rstd, w ? ld1(w + c) : 1.0f, bias, &a, &s);
-    const int64_t nvp = g.HW / V;
     const bool sc1_ok = plane_sc1_ok<T>(g);
-    // Vectors in flight per thread: 8, or 4 for the 16-bit training apply
-    // (bf16 GELU BatchNorm2d 256x64x112x112: 125.7 -> 123.0 us; the float32
-    // apply measured flat at 4, the eval apply keeps 8).
-    constexpr int U = (sizeof(T) == 2 && MODE == 0) ? 4 : kBnUnrollStream;
 
     for (int64_t n = n0; n < n1; ++n) {
         const int64_t off = plane_offset(g, n, c);
         for (int64_t v0 = threadIdx.x; v0 < nvp; v0 += (int64_t)kBnBlock * U) {
-            raw_t rx[U], rr[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t v = v0 + (int64_t)u * kBnBlock;
-                if (v < nvp) {
-                    rx[u] = vload_stream<T, V>(x + off + v * V);
-                    if (RES) rr[u] = vload_stream<T, V>(res + off + v * V);
-                }
-            }
+            if (!loaded) load(off, v0);  // else: the first plane's first vectors, loaded above
+            loaded = false;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int64_t v = v0 + (int64_t)u * kBnBlock;
@@ -308,6 +318,7 @@ bn_apply_kernel(const T *__restrict__ x, const T *__restrict__ res, const T *__r
                 }
             }
         }
+        loaded = false;  // a thread past the first plane's last vector did not use it
     }
 }
 
@@ -475,6 +486,26 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
     constexpr bool kFast = kFastGrad<T>;
     int c; int64_t n0, n1;
     tile_of_block(g, &c, &n0, &n1);
+    const int64_t nvp = g.HW / V;
+    const T *dzsrc = DZ_SRC == 1 ? dres : dy;
+    raw_t rd[kBnUnrollStream], rx[kBnUnrollStream], rr[kBnUnrollStream];
+    auto load = [&](int64_t off, int64_t v0) {
+#pragma unroll
+        for (int u = 0; u < kBnUnrollStream; ++u) {
+            const int64_t v = v0 + (int64_t)u * kBnBlock;
+            if (v < nvp) {
+                rd[u] = vload_stream<T, V>(dzsrc + off + v * V);
+                rx[u] = vload_stream<T, V>(x + off + v * V);
+                if (DZ_SRC == 2 && RES) rr[u] = vload_stream<T, V>(res + off + v * V);
+            }
+        }
+    };
+    // Float32 I/O: the block's first vectors are requested before the
+    // channel's sums are added, so that read overlaps them (dx 88.4 -> 86.3
+    // us on the float32 BatchNorm2d workload; the 16-bit dx kernel measured
+    // far slower with it, 181 -> 242 us).
+    bool loaded = sizeof(T) == 4 && n0 < n1;
+    if (loaded) load(plane_offset(g, n0, c), threadIdx.x);
     double sums[3];
     sum_channel_tiles(part, c, g.tiles, sums);
     const float mean = save_mean[c];
@@ -497,23 +528,13 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
         a *= kGeluWScale;
         s *= kGeluWScale;
     }
-    const int64_t nvp = g.HW / V;
     const bool sc1_ok = plane_sc1_ok<T>(g);
-    const T *dzsrc = DZ_SRC == 1 ? dres : dy;
 
     for (int64_t n = n0; n < n1; ++n) {
         const int64_t off = plane_offset(g, n, c);
         for (int64_t v0 = threadIdx.x; v0 < nvp; v0 += (int64_t)kBnBlock * kBnUnrollStream) {
-            raw_t rd[kBnUnrollStream], rx[kBnUnrollStream], rr[kBnUnrollStream];
-#pragma unroll
-            for (int u = 0; u < kBnUnrollStream; ++u) {
-                const int64_t v = v0 + (int64_t)u * kBnBlock;
-                if (v < nvp) {
-                    rd[u] = vload_stream<T, V>(dzsrc + off + v * V);
-                    rx[u] = vload_stream<T, V>(x + off + v * V);
-                    if (DZ_SRC == 2 && RES) rr[u] = vload_stream<T, V>(res + off + v * V);
-                }
-            }
+            if (!loaded) load(off, v0);  // else: the first plane's first vectors, loaded above
+            loaded = false;
 #pragma unroll
             for (int u = 0; u < kBnUnrollStream; ++u) {
                 const int64_t v = v0 + (int64_t)u * kBnBlock;
@@ -536,6 +557,7 @@ bn_bwd_dx_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__r
                 }
             }
         }
+        loaded = false;  // a thread past the first plane's last vector did not use it
     }
 }
 
