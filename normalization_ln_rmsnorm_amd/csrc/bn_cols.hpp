@@ -188,10 +188,10 @@ bn_col_stats_kernel(const T *__restrict__ x, BnColGeom g, double *__restrict__ p
 
 // ------------------------------------------- forward: channel statistics
 // One wave per channel.  Entry (tile, column) holds the n_t rows of the
-// tile as (mean, M2).  Each lane folds its entries (four loads in flight)
-// with Chan's pairwise merge in float64, then the lanes are merged by a
-// butterfly (the merge is symmetric, so every lane ends with the same
-// bits); one pass over the entries, in a fixed order.  (T is only the
+// tile as (mean, M2).  The lanes sum n_t and n_t mean_t over their entries
+// (up to eight each held in registers, else two passes over the entries),
+// one division gives the channel mean, and a second sum adds M2_t + n_t
+// (mean_t - mean)^2, all in float64 and in a fixed order.  (T is only the
 // dtype of the operation, so each dtype's translation unit has its own
 // instance.)
 template <typename T>
@@ -199,32 +199,66 @@ __global__ void __launch_bounds__(kBnBlock)
 bn_col_finalize_kernel(const double *__restrict__ part, BnColGeom g, float eps, float momentum,
                        float *__restrict__ running_mean, float *__restrict__ running_var,
                        float *__restrict__ save_mean, float *__restrict__ save_rstd) {
-    constexpr int U = 4;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t c = (int64_t)blockIdx.x * kBnWaves + threadIdx.x / kWave;
     if (c >= g.C) return;  // the whole wave leaves; no barrier follows
     const int64_t ne = (int64_t)g.T * g.HW;
-    WelfD acc{0.0, 0.0, 0.0};
-    for (int64_t e0 = lane; e0 < ne; e0 += (int64_t)kWave * U) {
-        double nt[U], m[U], q[U];
+    // Entry e: tile e / HW (its row count), column c HW + e mod HW.
+    auto entry = [&](int64_t e, double &nt, double &m, double &q) {
+        const int64_t t = e / g.HW, j = c * g.HW + e % g.HW;
+        const int64_t left = g.Nb - t * g.RT;
+        nt = (double)(left < g.RT ? left : g.RT);
+        m = part[(t * g.K + j) * 2];
+        q = part[(t * g.K + j) * 2 + 1];
+    };
+    // The exact parallel-axis identity, mean = sum n_t m_t / n and M2 =
+    // sum [M2_t + n_t (m_t - mean)^2], in a fixed order: one division per
+    // channel instead of one per pairwise merge (a chain of dependent
+    // float64 divisions per lane).
+    double sn = 0.0, snm = 0.0, m2 = 0.0;
+    constexpr int R = 8;  // entries held per lane on the one-round path
+    if (ne <= (int64_t)R * kWave) {  // the same in every lane
+        double nt[R], m[R], q[R];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t e = e0 + (int64_t)u * kWave;
-            nt[u] = m[u] = q[u] = 0.0;
-            if (e < ne) {
-                const int64_t t = e / g.HW, j = c * g.HW + e % g.HW;
-                const int64_t left = g.Nb - t * g.RT;
-                nt[u] = (double)(left < g.RT ? left : g.RT);
-                m[u] = part[(t * g.K + j) * 2];
-                q[u] = part[(t * g.K + j) * 2 + 1];
-            }
+        for (int r = 0; r < R; ++r) {
+            const int64_t e = lane + (int64_t)r * kWave;
+            nt[r] = m[r] = q[r] = 0.0;
+            if (e < ne) entry(e, nt[r], m[r], q[r]);
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) acc = welf_merge(acc, WelfD{nt[u], m[u], q[u]});
-    }
+        for (int r = 0; r < R; ++r) {
+            sn += nt[r];
+            snm = fma(nt[r], m[r], snm);
+        }
+        sn = wave_sum_dpp_d(sn);
+        snm = wave_sum_dpp_d(snm);
+        const double mean = sn > 0.0 ? snm / sn : 0.0;
 #pragma unroll
-    for (int s = kWave / 2; s >= 1; s >>= 1)
-        acc = welf_merge(acc, WelfD{shfl_xor_d(acc.n, s), shfl_xor_d(acc.mean, s), shfl_xor_d(acc.m2, s)});
+        for (int r = 0; r < R; ++r) {  // absent entries have n = M2 = 0
+            const double d = m[r] - mean;
+            m2 += fma(nt[r] * d, d, q[r]);
+        }
+        m2 = wave_sum_dpp_d(m2);
+        if (lane == 0) bn_save_stats(WelfD{sn, mean, m2}, c, eps, momentum, running_mean, running_var, save_mean, save_rstd);
+        return;
+    }
+    for (int64_t e = lane; e < ne; e += kWave) {
+        double nt, m, q;
+        entry(e, nt, m, q);
+        sn += nt;
+        snm = fma(nt, m, snm);
+    }
+    sn = wave_sum_dpp_d(sn);
+    snm = wave_sum_dpp_d(snm);
+    const double mean = sn > 0.0 ? snm / sn : 0.0;
+    for (int64_t e = lane; e < ne; e += kWave) {
+        double nt, m, q;
+        entry(e, nt, m, q);
+        const double d = m - mean;
+        m2 += fma(nt * d, d, q);
+    }
+    m2 = wave_sum_dpp_d(m2);
+    const WelfD acc{sn, mean, m2};
     if (lane == 0) bn_save_stats(acc, c, eps, momentum, running_mean, running_var, save_mean, save_rstd);
 }
 
