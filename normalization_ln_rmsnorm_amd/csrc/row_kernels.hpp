@@ -471,8 +471,9 @@ row_bwd_kernel(const T *__restrict__ dy, const T *__restrict__ x, const T *__res
     }
 
     // Combine the row slots of this block column by column and write one
-    // partial row per block.  LDS layout [element][thread] avoids bank
-    // conflicts; slots are added in increasing order.
+    // partial row per block (dW, and dB when wanted); slots are added in
+    // increasing order.  Partial rows go out through 16-byte device-scope
+    // stores where the width allows.
     if (!part_w && !part_b && !dw_out && !db_out) return;
     if (rpb == 1) {  // one row slot: every thread owns distinct columns
 #pragma unroll
