@@ -135,13 +135,14 @@ def test_unaligned_scalar_path(orc, kind):
 @pytest.mark.parametrize("kind", ["ln", "rms"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("M,N,ws_shift", [(1100, 130, 0), (2000, 256, 4), (777, 1003, 8), (600, 4096, 4),
-                                           (600, 8192, 0), (300, 8193, 0)])
+                                           (600, 8192, 0), (300, 8193, 0), (1000, 2048, 0)])
 def test_column_sum_paths(orc, kind, dtype, M, N, ws_shift):
     """dw / db through the column-sum kernel: many partial rows, widths that
     are not a multiple of 4 (scalar columns), workspaces that are not 16-byte
     aligned (scalar loads), and rows wide enough that a block holds a single
     row slot (its partial row stored straight from registers: 16 bytes at a
-    time, or one float at a time on the scalar path of an odd width),
+    time, or one float at a time on the scalar path of an odd width), and a
+    bf16 LayerNorm width whose dW and dB staging fills 64 KiB of LDS,
     checked against the oracle."""
     print(f"case colsum {kind} {dtype} {M}x{N} ws+{ws_shift}", flush=True)
     wl = _wl(kind, dtype)
